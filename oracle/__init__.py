@@ -1,0 +1,12 @@
+"""fp64 CPU oracle for paged attention (test infrastructure only; see
+``oracle.attention`` for what may import it)."""
+from .attention import (  # noqa: F401
+    attend,
+    block_of,
+    gather,
+    kv_head_of,
+    paged_decode,
+    paged_prefill_chunk,
+    query_position,
+    reshape_and_cache,
+)
