@@ -1,0 +1,444 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: the slot-mapped cache
+write of the step's new tokens, then decode (partition kernel + reduce
+kernel) and, for the mixed workload, the prefill chunk.  The headline line is
+the Llama-2-7B-like decode workload (128 sequences, 32/32 heads, head_dim 128,
+fp16, contexts U[512, 4096], 512-token partitions); the other four workloads
+are measured the same way and reported under "workloads".
+
+Timing: HIP events on the stream the kernels run on (torch's current stream),
+one pair per kernel, K timed steps after W warm-up steps.  Between steps, and
+outside the events, a 512 MiB fill evicts the L2s and the 256 MB last-level
+cache so that every step reads its K/V from HBM.
+
+Figures:
+  value          algorithmic bytes of one step / step time (GB/s); algorithmic
+                 bytes count every attended K/V token of each physical block
+                 once, plus Q, output, block-table entries, context lengths and
+                 the cache write (new K/V read + written, slots);
+  roofline       the decode partition kernel alone: its algorithmic bytes / its
+                 average event-timed duration, against 8 TB/s;
+  cpu_baseline   the fp64 oracle (tests' reference implementation, untuned) on a
+                 bounded sample of the same workload, one host thread.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
+       python bench.py --profile-kernel NAME    (a few launches, for rocprofv3)
+       python bench.py --copy-probe              (1 GiB device copy, counter scale)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix, published
+HEADLINE = "llama2_7b"
+METRIC = "paged-attn decode achieved HBM GB/s (% of MI355X peak) + attended tokens/s"
+FLUSH_BYTES = 512 << 20
+DTYPE_NAME = {"fp32": "f32", "fp16": "f16", "bf16": "bf16"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic work of one step (host arithmetic on the workload's tables).
+# ---------------------------------------------------------------------------
+def _attended_slots(w, rows):
+    bs = w.block_size
+    parts = []
+    for s in rows:
+        C = int(w.context_lens[s])
+        t = np.arange(C, dtype=np.int64)
+        parts.append(w.block_tables[s, t // bs].astype(np.int64) * bs + t % bs)
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def work(w):
+    """Bytes and flops of one step, split by kernel."""
+    eb = w.elem_bytes
+    row_kv = w.num_kv_heads * w.head_dim * eb * 2  # K + V of one token, all KV heads
+    qrow = w.num_heads * w.head_dim * eb
+    bs = w.block_size
+    out = {}
+    dec = w.decode_rows
+    ctx = w.context_lens.astype(np.int64)
+    if len(dec):
+        uniq = len(np.unique(_attended_slots(w, dec)))
+        logical = int(ctx[dec].sum())
+        tbl = int(((ctx[dec] + bs - 1) // bs).sum()) * 4 + len(dec) * 4
+        single = int((ctx[dec] <= w.partition_size).sum())
+        out["decode_kv_bytes"] = uniq * row_kv
+        out["decode_logical_kv_bytes"] = logical * row_kv
+        out["decode_bytes"] = uniq * row_kv + 2 * len(dec) * qrow + tbl
+        out["partition_kernel_bytes"] = uniq * row_kv + len(dec) * qrow + tbl + single * qrow
+        out["decode_attended_tokens"] = logical
+    if len(w.prefill_rows):
+        pre = w.prefill_rows
+        uniq = len(np.unique(_attended_slots(w, pre)))
+        nq = int(w.query_start_loc[-1])
+        pairs = 0
+        for i, r in enumerate(pre):
+            L = int(w.query_start_loc[i + 1] - w.query_start_loc[i])
+            C = int(ctx[r])
+            pairs += L * (C - L) + L * (L + 1) // 2
+        out["prefill_bytes"] = uniq * row_kv + 2 * nq * qrow
+        out["prefill_flops"] = pairs * w.num_heads * 4 * w.head_dim
+        out["prefill_attended_pairs"] = pairs
+    n_new = len(w.slot_mapping)
+    out["write_bytes"] = 2 * n_new * row_kv + 8 * n_new
+    out["step_bytes"] = out.get("decode_bytes", 0) + out.get("prefill_bytes", 0) + out["write_bytes"]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Device state of one workload and its step.
+# ---------------------------------------------------------------------------
+class Step:
+    def __init__(self, w, dev):
+        import paged_kv_cache_179_amd as pa
+
+        self.pa = pa
+        self.w = w
+        self.dev = dev
+        self.kc0 = w.key_cache.to(dev)
+        self.vc0 = w.value_cache.to(dev)
+        self.kc = self.kc0  # the step writes into the pool in place (same slots every step)
+        self.vc = self.vc0
+        self.nk = w.new_key.to(dev)
+        self.nv = w.new_value.to(dev)
+        self.slots = torch.from_numpy(w.slot_mapping).to(dev)
+        bt = torch.from_numpy(w.block_tables)
+        cl = torch.from_numpy(w.context_lens)
+        dr = torch.from_numpy(w.decode_rows)
+        pr = torch.from_numpy(w.prefill_rows)
+        self.bt_d = bt[dr].contiguous().to(dev)
+        self.cl_d = cl[dr].contiguous().to(dev)
+        self.bt_p = bt[pr].contiguous().to(dev)
+        self.cl_p = cl[pr].contiguous().to(dev)
+        self.q_d = w.query_decode.to(dev)
+        self.q_p = w.query_prefill.to(dev)
+        self.qsl = torch.from_numpy(w.query_start_loc).to(dev)
+        self.out_d = torch.empty_like(self.q_d)
+        self.out_p = torch.empty_like(self.q_p)
+        self.has_dec = len(w.decode_rows) > 0
+        self.has_pre = len(w.prefill_rows) > 0
+        self.maxc_d = int(w.context_lens[w.decode_rows].max()) if self.has_dec else 0
+        self.maxc_p = int(w.context_lens[w.prefill_rows].max()) if self.has_pre else 0
+        self.maxq = int(np.diff(w.query_start_loc).max()) if self.has_pre else 0
+        nb = pa.decode_workspace_bytes(len(w.decode_rows), w.num_heads, w.head_dim,
+                                       self.maxc_d, w.partition_size) if self.has_dec else 0
+        self.ws_d = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+        nbp = pa.prefill_workspace_bytes(int(w.query_start_loc[-1]), len(w.prefill_rows),
+                                         w.num_heads, w.num_kv_heads, w.head_dim, self.maxq,
+                                         self.maxc_p) if self.has_pre else 0
+        self.ws_p = torch.empty(max(nbp, 256), dtype=torch.uint8, device=dev)
+
+    def write(self):
+        self.pa.reshape_and_cache(self.nk, self.nv, self.kc, self.vc, self.slots)
+
+    def partitions(self):
+        self.pa.decode_partitions(self.out_d, self.q_d, self.kc, self.vc, self.bt_d, self.cl_d,
+                                  self.w.scale, self.maxc_d, partition_size=self.w.partition_size,
+                                  workspace=self.ws_d)
+
+    def reduce(self):
+        w = self.w
+        self.pa.decode_reduce(self.out_d, self.cl_d, w.num_heads, w.head_dim,
+                              w.max_blocks_per_seq, w.block_size, self.maxc_d, w.partition_size,
+                              self.ws_d)
+
+    def prefill(self):
+        self.pa.prefill_chunk(self.out_p, self.q_p, self.qsl, self.kc, self.vc, self.bt_p,
+                              self.cl_p, self.w.scale, self.maxq, self.maxc_p, workspace=self.ws_p)
+
+    def phases(self):
+        ph = [("write", self.write)]
+        if self.has_pre:
+            ph.append(("prefill", self.prefill))
+        if self.has_dec:
+            ph += [("partitions", self.partitions), ("reduce", self.reduce)]
+        return ph
+
+
+def measure(step, steps, warmup, flush_buf):
+    """Event-timed phases over `steps` steps (after `warmup`); returns ms lists."""
+    phases = step.phases()
+    for _ in range(warmup):
+        flush_buf.zero_()
+        for _, fn in phases:
+            fn()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        flush_buf.zero_()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+        e[0].record()
+        for i, (_, fn) in enumerate(phases):
+            fn()
+            e[i + 1].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    res = {name: [] for name, _ in phases}
+    res["step"] = []
+    for e in evs:
+        for i, (name, _) in enumerate(phases):
+            res[name].append(e[i].elapsed_time(e[i + 1]))
+        res["step"].append(e[0].elapsed_time(e[-1]))
+    res["_wall_s"] = wall
+    return res
+
+
+def summarize(name, w, wk, t, steps):
+    mean = {k: float(np.mean(v)) for k, v in t.items() if not k.startswith("_")}
+    r = {"workload": name, "dtype": DTYPE_NAME[w.dtype], "num_seqs": w.num_seqs,
+         "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+         "block_size": w.block_size, "partition_size": w.partition_size,
+         "ms": {k: round(v, 5) for k, v in mean.items()},
+         "step_bytes": wk["step_bytes"],
+         "step_gbs": wk["step_bytes"] / (mean["step"] * 1e-3) / 1e9}
+    if "partitions" in mean:
+        dec_ms = mean["partitions"] + mean["reduce"]
+        r["decode_ms"] = dec_ms
+        r["decode_gbs"] = wk["decode_bytes"] / (dec_ms * 1e-3) / 1e9
+        r["decode_hbm_frac"] = r["decode_gbs"] / HBM_PEAK_GBS
+        r["decode_effective_gbs"] = (wk["decode_logical_kv_bytes"] + wk["decode_bytes"]
+                                     - wk["decode_kv_bytes"]) / (dec_ms * 1e-3) / 1e9
+        r["decode_attended_tokens_per_s"] = wk["decode_attended_tokens"] / (dec_ms * 1e-3)
+        r["partition_kernel_gbs"] = wk["partition_kernel_bytes"] / (mean["partitions"] * 1e-3) / 1e9
+        r["decode_bytes"] = wk["decode_bytes"]
+    if "prefill" in mean:
+        r["prefill_tflops"] = wk["prefill_flops"] / (mean["prefill"] * 1e-3) / 1e12
+        r["prefill_mfma_frac"] = r["prefill_tflops"] / MFMA_BF16_PEAK_TFLOPS
+        r["prefill_flops"] = wk["prefill_flops"]
+    r["write_gbs"] = wk["write_bytes"] / (mean["write"] * 1e-3) / 1e9
+    return r
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample (one host thread).
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, budget_s=15.0):
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    def f64(t):
+        return t.to(torch.float64).numpy()
+
+    # Caches after the step's write, as the oracle computes it (raw bits).
+    raw = {torch.float16: torch.int16, torch.bfloat16: torch.int16, torch.float32: torch.int32}[
+        w.key_cache.dtype]
+    kc, vc = oracle.reshape_and_cache(w.new_key.view(raw).numpy(), w.new_value.view(raw).numpy(),
+                                      w.key_cache.view(raw).numpy(), w.value_cache.view(raw).numpy(),
+                                      w.slot_mapping, w.block_size)
+    kc = torch.from_numpy(kc).view(w.key_cache.dtype)
+    vc = torch.from_numpy(vc).view(w.key_cache.dtype)
+    eb = w.elem_bytes
+    row_kv = w.num_kv_heads * w.head_dim * eb * 2
+    qrow = w.num_heads * w.head_dim * eb
+    done_rows = []
+    t_used = 0.0
+    with threadpool_limits(limits=1):
+        for i, s in enumerate(w.decode_rows):
+            C = int(w.context_lens[s])
+            nblk = (C + w.block_size - 1) // w.block_size
+            blocks = torch.from_numpy(w.block_tables[s, :nblk].astype(np.int64))
+            # only the blocks this sequence reads, converted once
+            kb = kc[blocks]
+            vb = vc[blocks]
+            local = np.arange(nblk)
+            q = f64(w.query_decode[i:i + 1])
+            t0 = time.perf_counter()
+            oracle.paged_decode(q, f64(kb), f64(vb), local[None], [C], w.scale, w.block_size)
+            t_used += time.perf_counter() - t0
+            done_rows.append(int(s))
+            if t_used >= budget_s:
+                break
+    toks = int(w.context_lens[done_rows].astype(np.int64).sum())
+    nbytes = toks * row_kv + 2 * len(done_rows) * qrow
+    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "attended_tokens_per_s": toks / t_used, "seconds": round(t_used, 3),
+            "sample": f"oracle decode of the first {len(done_rows)} of {len(w.decode_rows)} "
+                      f"sequences ({toks} attended tokens), fp64 numpy, 1 thread",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# ---------------------------------------------------------------------------
+# Counter-derived traffic (committed rocprofv3 summaries).
+# ---------------------------------------------------------------------------
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "paged_kv_cache_179_amd", "csrc"))):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(ROOT, "paged_kv_cache_179_amd", "csrc", f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload):
+    """HBM bytes per partition-kernel launch from the committed counter summary,
+    or None if there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"pmc_decode_partition_{workload}.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def profile_kernel(name, launches=5):
+    from paged_kv_cache_179_amd import workloads as W
+
+    w = W.make(name)
+    st = Step(w, torch.device("cuda:0"))
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
+    st.write()
+    for _ in range(launches):
+        flush.zero_()
+        if st.has_dec:
+            st.partitions()
+            st.reduce()
+        if st.has_pre:
+            st.prefill()
+    torch.cuda.synchronize()
+    log(f"profiled {launches} launches of {name}")
+
+
+def copy_probe(nbytes=1 << 30, launches=3):
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {nbytes} bytes x {launches}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--only", default=None, help="measure one workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-kernel", default=None)
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode shards by sequence or KV head with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import paged_kv_cache_179_amd as pa
+
+    if not pa.library_path().exists():
+        from paged_kv_cache_179_amd.build import build
+
+        build()
+    pa.library()
+    if args.copy_probe:
+        copy_probe()
+        return
+    if args.profile_kernel:
+        profile_kernel(args.profile_kernel)
+        return
+
+    from paged_kv_cache_179_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    names = [args.only] if args.only else W.NAMES
+    if HEADLINE not in names:
+        names = names + [HEADLINE]
+    results = {}
+    headline = None
+    for name in names:
+        t0 = time.perf_counter()
+        w = W.make(name)
+        log(f"{name}: generated in {time.perf_counter() - t0:.1f}s")
+        st = Step(w, dev)
+        wk = work(w)
+        t = measure(st, args.steps, args.warmup, flush)
+        r = summarize(name, w, wk, t, args.steps)
+        r["wall_ms_per_step_incl_flush"] = t["_wall_s"] / args.steps * 1e3
+        results[name] = r
+        log(f"{name}: " + json.dumps({k: r[k] for k in r if k.endswith(("gbs", "frac", "_ms", "tflops"))}))
+        if name == HEADLINE:
+            headline = (w, wk, t, r)
+            if not args.no_cpu_baseline:
+                log("cpu baseline ...")
+                results["_cpu"] = cpu_baseline(w)
+        del st
+        torch.cuda.empty_cache()
+
+    w, wk, t, r = headline
+    part_ms = float(np.mean(t["partitions"]))
+    achieved = wk["partition_kernel_bytes"] / (part_ms * 1e-3) / 1e9
+    traffic = counter_traffic(HEADLINE)
+    line = {
+        "metric": METRIC,
+        "value": round(r["step_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"]["step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE_NAME[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": "llama2_7b_decode_step", "num_seqs": w.num_seqs,
+                   "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size,
+                   "context_lens": "uniform[512,4096]", "partition_size": w.partition_size,
+                   "num_blocks": w.num_blocks},
+        "hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
+        "attended_tokens_per_s": round(r["decode_attended_tokens_per_s"], 1),
+        "roofline": {"kernel": "decode_partition_kernel", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "avg_launch_ms": round(part_ms, 5),
+                     "algorithmic_bytes_per_launch": wk["partition_kernel_bytes"]},
+        "cpu_baseline": results.get("_cpu"),
+        "workloads": {k: v for k, v in results.items() if not k.startswith("_")},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

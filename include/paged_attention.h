@@ -1,0 +1,182 @@
+/*
+ * paged_attention.h -- C ABI of the MI355X (gfx950) paged-attention library.
+ *
+ * The operation: each query token attends to the keys and values of its own
+ * sequence, which sit in fixed-size physical blocks of a shared pool and are
+ * reached through a per-sequence block table (mini-vLLM README, "How it works
+ * -- Paged KV-cache").  Three operations make up the path:
+ *
+ *   pa_reshape_and_cache  write the new tokens' K/V into their pool slots
+ *                         (mini-vLLM README, "End-to-end throughput vs
+ *                         baselines": K/V writes as one indexed assignment);
+ *   pa_decode             one query token per sequence attends its whole
+ *                         context (wLLM PyPI page, "Features -- Core engine":
+ *                         the PagedAttention kernel over a block-based cache),
+ *                         split into context partitions plus a merge;
+ *   pa_prefill_chunk      a chunk of a prompt attends the cached context before
+ *                         it and itself causally (wLLM PyPI page, "Features --
+ *                         Core engine": chunked prefill).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array arguments are DEVICE pointers into memory the caller owns; the
+ *   library allocates nothing and keeps no state between calls.  Every call
+ *   only enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
+ *   returns; results are ready when the stream reaches that point.
+ * - Element type `dtype` is shared by query, key/value, caches and output.
+ * - Cache layout (K and V alike): [num_blocks][num_kv_heads][block_size][head_dim],
+ *   contiguous.  Token t of a sequence lives in block table[t / block_size]
+ *   at offset t % block_size.  Query/key/value/output are contiguous
+ *   [tokens][heads][head_dim].
+ * - Grouped-query heads: query head h reads KV head h / (num_heads /
+ *   num_kv_heads) (contiguous groups; mini-vLLM's GQA-aware kernel maps each
+ *   query head to its KV head instead of expanding K/V).
+ * - Supported: head_dim 64, 128 or 256; block_size a power of two 1..256;
+ *   dtype F32, F16 or BF16 (prefill: F16 or BF16).  Softmax and accumulation
+ *   run in fp32; outputs are rounded to `dtype` to nearest-even.
+ * - Host-side arguments are validated before anything is launched and a bad
+ *   one returns an error status with nothing enqueued.  Device arrays are NOT
+ *   inspected (that would need a synchronisation).  Their contents are
+ *   preconditions: block ids in [0, num_blocks), context_lens in
+ *   [0, min(max_context_len, max_blocks_per_seq * block_size)], slots unique.
+ *   Kernels clamp every index to the buffers they were given, so violating a
+ *   precondition gives wrong numbers, never an out-of-bounds access: a slot or
+ *   block id outside the pool is skipped (write) or replaced by block 0
+ *   (read); lengths are clamped to the limits above.
+ * - Launch failures are reported as PA_ERR_LAUNCH.
+ */
+#ifndef PAGED_ATTENTION_H_
+#define PAGED_ATTENTION_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL_POINTER = 1,
+  PA_ERR_BAD_SHAPE = 2,
+  PA_ERR_UNSUPPORTED = 3,
+  PA_ERR_WORKSPACE_TOO_SMALL = 4,
+  PA_ERR_LAUNCH = 5
+} pa_status;
+
+typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
+
+/* Static string naming a status code ("unknown status" for other values). */
+const char* pa_status_str(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int pa_version(void);
+
+/*
+ * Slot-mapped cache write.  For every n < num_tokens with
+ * s = slot_mapping[n] >= 0:  key_cache[s / block_size][h][s % block_size][:] =
+ * key[n][h][:] and the same for value, for every KV head h.  A pure bit copy.
+ *   key, value          [num_tokens][num_kv_heads][head_dim]
+ *   key_cache, value_cache [num_blocks][num_kv_heads][block_size][head_dim]
+ *   slot_mapping        int64 [num_tokens]; negative = skip this token;
+ *                       slots >= num_blocks * block_size are skipped too.
+ * num_tokens == 0 is a valid no-op.  Duplicate slots: which write lands is
+ * unspecified.
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int64_t* slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                               void* stream);
+
+/*
+ * Workspace bytes pa_decode needs: 0 when no sequence can span more than one
+ * partition (partition_size == 0 or max_context_len <= partition_size), else
+ * num_seqs * num_heads * ceil(max_context_len / partition_size) partial
+ * results of (head_dim + 2) floats, each array 256-byte aligned.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Decode attention: row s of `query` is the token at position
+ * context_lens[s] - 1 of sequence s and attends all context_lens[s] cached
+ * tokens of that sequence (the current token's K/V must already be written).
+ *   out, query      [num_seqs][num_heads][head_dim]
+ *   block_tables    int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens    int32 [num_seqs]; 0 gives an all-zero output row
+ *   max_context_len host-side upper bound of context_lens; sizes the grid
+ *   scale           multiplies q.k before the softmax (e.g. 1/sqrt(head_dim))
+ *   partition_size  tokens per context partition; 0 = never split.  Otherwise
+ *                   a positive multiple of 64 and of block_size.  Sequences
+ *                   longer than one partition are processed by several
+ *                   workgroups whose partial softmax states are merged by a
+ *                   second kernel through `workspace`.
+ *   workspace       device scratch of >= pa_decode_workspace_bytes(...) bytes
+ *                   (may be NULL when that is 0); overwritten, no alignment
+ *                   requirement beyond 256 bytes.
+ */
+pa_status pa_decode(void* out, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                    float scale, int32_t partition_size, void* workspace,
+                    size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/*
+ * The two halves of pa_decode, for callers that time or schedule them apart
+ * (pa_decode == pa_decode_partitions followed by pa_decode_reduce on the same
+ * stream with the same arguments).  pa_decode_partitions writes the output of
+ * every sequence that fits one partition and the partial softmax states of
+ * the others into `workspace`; pa_decode_reduce merges those partial states
+ * (log-sum-exp weighted) into `out` and leaves the other rows untouched.
+ */
+pa_status pa_decode_partitions(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               int32_t max_context_len, float scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                               void* stream);
+
+pa_status pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                           int32_t block_size, int32_t max_context_len,
+                           int32_t partition_size, const void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/*
+ * Workspace bytes pa_prefill_chunk needs for these sizes (0 if none).
+ */
+size_t pa_prefill_workspace_bytes(int32_t num_q_tokens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_query_len, int32_t max_context_len);
+
+/*
+ * Chunked-prefill attention.  Sequence s owns query rows
+ * query_start_loc[s] .. query_start_loc[s+1]-1 (L rows, L may be 1) and a
+ * context of context_lens[s] tokens that already includes those L tokens (their
+ * K/V must be written first).  Row i sits at position C - L + i and attends
+ * keys 0 .. C - L + i: the causal mask is aligned to the end of the context.
+ *   out, query       [num_q_tokens][num_heads][head_dim]
+ *   query_start_loc  int32 [num_seqs + 1], non-decreasing, last = num_q_tokens
+ *   max_query_len    host-side upper bound of the chunk lengths (grid size)
+ *   other arguments  as for pa_decode.  Rows of a sequence with L > C are
+ *                    preconditions violations (their keys are clamped to C).
+ */
+pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_start_loc,
+                           int32_t num_q_tokens, int32_t max_query_len, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_context_len, float scale, void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_H_ */

@@ -1,0 +1,231 @@
+"""ctypes binding of ``libpaged_attention.so`` (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, checks their
+dtype/shape/contiguity, and passes raw device pointers plus the current HIP
+stream to the C ABI declared in ``include/paged_attention.h``.  No arithmetic
+of the method happens here, and there is no fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+_LIB_NAME = "libpaged_attention.so"
+_lib = None
+
+PA_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+_c_ptr = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_size = ctypes.c_size_t
+_f32 = ctypes.c_float
+
+_SIGNATURES = {
+    "pa_status_str": ([ctypes.c_int], ctypes.c_char_p),
+    "pa_version": ([], ctypes.c_int),
+    "pa_reshape_and_cache": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _i32, _i32, _i32, _i32,
+                              ctypes.c_int, _c_ptr], ctypes.c_int),
+    "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32], _size),
+    "pa_decode": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32, _i32, _i32,
+                   _i32, _i32, _i32, _f32, _i32, _c_ptr, _size, ctypes.c_int, _c_ptr],
+                  ctypes.c_int),
+    "pa_decode_partitions": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32,
+                              _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_ptr, _size,
+                              ctypes.c_int, _c_ptr], ctypes.c_int),
+    "pa_decode_reduce": ([_c_ptr, _c_ptr, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _c_ptr, _size,
+                          ctypes.c_int, _c_ptr], ctypes.c_int),
+    "pa_prefill_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _size),
+    "pa_prefill_chunk": ([_c_ptr, _c_ptr, _c_ptr, _i32, _i32, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr,
+                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _c_ptr, _size,
+                          ctypes.c_int, _c_ptr], ctypes.c_int),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+class PagedAttentionError(RuntimeError):
+    """A C-ABI call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {message} (status {status})")
+        self.status = status
+
+
+def library_path() -> Path:
+    return Path(os.environ.get("PA_LIBRARY", Path(__file__).resolve().parent / _LIB_NAME))
+
+
+def library():
+    """Load the shared library once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not path.exists():
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m paged_kv_cache_179_amd.build`")
+        lib = ctypes.CDLL(str(path))
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        msg = library().pa_status_str(status).decode()
+        raise PagedAttentionError(fn, status, msg)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t.data_ptr()
+
+
+def _cache_dims(key_cache: torch.Tensor, value_cache: torch.Tensor):
+    if key_cache.dim() != 4 or key_cache.shape != value_cache.shape:
+        raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_dim]")
+    if key_cache.dtype != value_cache.dtype:
+        raise TypeError("key_cache and value_cache dtypes differ")
+    nb, hkv, bs, d = key_cache.shape
+    return int(nb), int(hkv), int(bs), int(d)
+
+
+def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                      value_cache: torch.Tensor, slot_mapping: torch.Tensor) -> None:
+    """Write key/value [N, Hkv, D] into the caches at ``slot_mapping`` (int64 [N])."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    dt = key_cache.dtype
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim] matching the cache")
+    n = int(key.shape[0])
+    if tuple(slot_mapping.shape) != (n,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    st = library().pa_reshape_and_cache(
+        _dev(key, "key", dt), _dev(value, "value", dt), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
+        n, hkv, d, bs, nb, PA_DTYPE[dt], _stream(key_cache))
+    _check("pa_reshape_and_cache", st)
+
+
+def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,
+                           partition_size: int) -> int:
+    return int(library().pa_decode_workspace_bytes(num_seqs, num_heads, head_dim,
+                                                   max_context_len, partition_size))
+
+
+def _decode_common(out, query, key_cache, value_cache, block_tables, context_lens):
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    dt = key_cache.dtype
+    if query.dim() != 3 or query.shape[2] != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_seqs, num_heads, head_dim] matching the cache")
+    s, hq = int(query.shape[0]), int(query.shape[1])
+    if block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if tuple(context_lens.shape) != (s,):
+        raise ValueError("context_lens must be [num_seqs]")
+    ptrs = (_dev(out, "out", dt), _dev(query, "query", dt), _dev(key_cache, "key_cache"),
+            _dev(value_cache, "value_cache"), _dev(block_tables, "block_tables", torch.int32),
+            _dev(context_lens, "context_lens", torch.int32))
+    return ptrs, (nb, hkv, bs, d, s, hq, int(block_tables.shape[1]), dt)
+
+
+def _workspace(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=like.device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must hold {nbytes} bytes")
+    return workspace, _dev(workspace, "workspace")
+
+
+def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+           value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
+           scale: float, max_context_len: int, partition_size: int = 512,
+           workspace: Optional[torch.Tensor] = None, _fn: str = "pa_decode") -> None:
+    """Paged decode attention into ``out`` ([S, Hq, D]); see pa_decode."""
+    ptrs, (nb, hkv, bs, d, s, hq, mbps, dt) = _decode_common(out, query, key_cache, value_cache,
+                                                             block_tables, context_lens)
+    need = decode_workspace_bytes(s, hq, d, max_context_len, partition_size)
+    ws, ws_ptr = _workspace(need, out, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    fn = getattr(library(), _fn)
+    st = fn(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], mbps, ptrs[5], s, hq, hkv, d, bs, nb,
+            int(max_context_len), float(scale), int(partition_size), ws_ptr, nbytes,
+            PA_DTYPE[dt], _stream(out))
+    _check(_fn, st)
+    return ws
+
+
+def decode_partitions(*args, **kwargs):
+    """First half of pa_decode (partition kernel only); returns the workspace."""
+    return decode(*args, _fn="pa_decode_partitions", **kwargs)
+
+
+def decode_reduce(out: torch.Tensor, context_lens: torch.Tensor, num_heads: int, head_dim: int,
+                  max_blocks_per_seq: int, block_size: int, max_context_len: int,
+                  partition_size: int, workspace: Optional[torch.Tensor]) -> None:
+    """Second half of pa_decode: merge the partition states in ``workspace``."""
+    s = int(context_lens.shape[0])
+    dt = out.dtype
+    ws_ptr = None if workspace is None else _dev(workspace, "workspace")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = library().pa_decode_reduce(_dev(out, "out", dt), _dev(context_lens, "context_lens",
+                                                               torch.int32),
+                                    s, num_heads, head_dim, max_blocks_per_seq, block_size,
+                                    int(max_context_len), int(partition_size), ws_ptr, nbytes,
+                                    PA_DTYPE[dt], _stream(out))
+    _check("pa_decode_reduce", st)
+
+
+def prefill_workspace_bytes(num_q_tokens: int, num_seqs: int, num_heads: int, num_kv_heads: int,
+                            head_dim: int, max_query_len: int, max_context_len: int) -> int:
+    return int(library().pa_prefill_workspace_bytes(num_q_tokens, num_seqs, num_heads,
+                                                    num_kv_heads, head_dim, max_query_len,
+                                                    max_context_len))
+
+
+def prefill_chunk(out: torch.Tensor, query: torch.Tensor, query_start_loc: torch.Tensor,
+                  key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
+                  context_lens: torch.Tensor, scale: float, max_query_len: int,
+                  max_context_len: int, workspace: Optional[torch.Tensor] = None) -> None:
+    """Chunked-prefill attention into ``out`` ([num_q_tokens, Hq, D]); see pa_prefill_chunk."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    dt = key_cache.dtype
+    if query.dim() != 3 or query.shape[2] != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_q_tokens, num_heads, head_dim]")
+    nq, hq = int(query.shape[0]), int(query.shape[1])
+    s = int(context_lens.shape[0])
+    if tuple(query_start_loc.shape) != (s + 1,):
+        raise ValueError("query_start_loc must be [num_seqs + 1]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    need = prefill_workspace_bytes(nq, s, hq, hkv, d, max_query_len, max_context_len)
+    ws, ws_ptr = _workspace(need, out, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = library().pa_prefill_chunk(
+        _dev(out, "out", dt), _dev(query, "query", dt),
+        _dev(query_start_loc, "query_start_loc", torch.int32), nq, int(max_query_len),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), s, hq, hkv, d, bs, nb,
+        int(max_context_len), float(scale), ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
+    _check("pa_prefill_chunk", st)
+    return ws

@@ -1,0 +1,359 @@
+// Paged-attention decode for gfx950: one query token per sequence attends its
+// whole context, read block by block through the sequence's block table.
+//
+// The operation is the PagedAttention decode the wLLM PyPI page lists under
+// "Features -- Core engine" (a block-based KV cache read by a custom kernel),
+// with the grouped-query head mapping of the mini-vLLM README ("End-to-end
+// throughput vs baselines": each query head reads its KV head directly).
+//
+// Work decomposition.  One workgroup (4 waves) handles one
+// (sequence, KV head, context partition) and all query heads of that KV head
+// (up to 8; larger groups are split over several workgroups).  Its K/V bytes
+// are read exactly once per workgroup, whatever the group size.
+//
+// Inside a wave, a token's head_dim row is spread over LPT lanes that each
+// load 16 contiguous bytes, so one wave-wide load covers TPL = 64 / LPT whole
+// rows and every (block, head) run of the [block][head][offset][dim] pool is
+// read with fully coalesced 16-byte loads.  q.k is a per-lane packed dot
+// product (v_dot2 for 16-bit types) followed by a DPP butterfly over the LPT
+// lanes of the row.  Each lane keeps an online-softmax state (running max m,
+// denominator l, un-normalised accumulator) for its own token stream; the
+// states are merged across the wave, then across the 4 waves through LDS, at
+// the end of the partition.  The block ids of the partition are staged in LDS
+// (512 tokens' worth at a time), and so are the group's query rows.
+//
+// A sequence that fits one partition writes its output directly; longer ones
+// write (m, l, acc) per partition to the workspace and decode_reduce merges
+// them: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
+// Scores are kept in log2 units (scale * log2(e) folded in) so every
+// exponential is one v_exp_f32.
+#include "device_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = kDecodeThreads / kWave;
+
+template <typename E, int D>
+struct RowLayout {
+  static constexpr int kEpl = E::kPerGroup;       // elements per lane load
+  static constexpr int kLpt = D / kEpl;           // lanes per token row
+  static constexpr int kTpl = kWave / kLpt;       // token rows per wave load
+  static constexpr int kUnroll = kTpl >= 8 ? 2 : 4;  // wave loads per tile
+  static constexpr int kTile = kUnroll * kTpl;    // tokens per wave iteration
+  static_assert(kLpt >= 1 && kLpt <= kWave, "row must fit one wave");
+};
+
+template <typename E, int D, int GT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
+    DecodeArgs a, int32_t head_chunks, uint32_t n_logical, uint32_t per_xcd, float scale_log2) {
+  using R = RowLayout<E, D>;
+  constexpr int EPL = R::kEpl, LPT = R::kLpt, TPL = R::kTpl, U = R::kUnroll, TILE = R::kTile;
+
+  __shared__ int32_t s_tbl[kSegTokens];
+  __shared__ u32x4 s_q[GT * LPT];
+  __shared__ float s_max[kWaves][GT];
+  __shared__ float s_sum[kWaves][GT];
+  __shared__ float s_acc[kWaves][GT][D];
+
+  // Logical order ((seq * Hkv + kv_head) * P + part) * chunks + chunk keeps one
+  // sequence's work on one XCD (its L2), in sequence order.
+  const uint32_t logical = xcd_remap(blockIdx.x, per_xcd);
+  if (logical >= n_logical) return;
+  uint32_t rem = logical;
+  const int chunk = rem % head_chunks;
+  rem /= head_chunks;
+  const int part = rem % a.num_parts;
+  rem /= a.num_parts;
+  const int kvh = rem % a.num_kv_heads;
+  const int seq = rem / a.num_kv_heads;
+
+  const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
+  const int nparts = max(1, (ctx + a.part_tokens - 1) / a.part_tokens);
+  if (part >= nparts) return;
+
+  const int group = a.num_heads / a.num_kv_heads;
+  const int h_first = kvh * group + chunk * GT;
+  const int nh = min(GT, group - chunk * GT);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int sub = lane % LPT;  // which 16-byte slice of the row
+  const int grp = lane / LPT;  // which token row of a wave load
+
+  // Stage the query rows of this head group, then take this lane's slice.
+  {
+    const u32x4* qsrc = reinterpret_cast<const u32x4*>(
+        static_cast<const char*>(a.query) +
+        (static_cast<int64_t>(seq) * a.num_heads + h_first) * D * E::kBytes);
+    for (int i = tid; i < GT * LPT; i += kDecodeThreads) {
+      const int h = i / LPT;
+      s_q[i] = (h < nh) ? qsrc[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
+  u32x4 q[GT];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) q[h] = s_q[h * LPT + sub];
+
+  float m[GT], l[GT], acc[GT][EPL];
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    m[h] = -__builtin_inff();
+    l[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  const int lbs = a.log2_block_size;
+  const int off_mask = (1 << lbs) - 1;
+  const char* kbase = static_cast<const char*>(a.key_cache);
+  const char* vbase = static_cast<const char*>(a.value_cache);
+  const int64_t row_bytes = static_cast<int64_t>(D) * E::kBytes;
+  const int64_t lane_bytes = static_cast<int64_t>(sub) * 16;
+  const int32_t* table = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+
+  const int tok_begin = part * a.part_tokens;
+  const int tok_end = min(tok_begin + a.part_tokens, ctx);
+  for (int seg = tok_begin; seg < tok_end; seg += kSegTokens) {
+    const int seg_end = min(seg + kSegTokens, tok_end);
+    const int first_blk = seg >> lbs;
+    const int nblk = ((seg_end - 1) >> lbs) - first_blk + 1;
+    __syncthreads();  // previous segment's ids are no longer read
+    for (int i = tid; i < nblk; i += kDecodeThreads) {
+      const int b = table[first_blk + i];
+      s_tbl[i] = (b < 0 || b >= a.num_blocks) ? 0 : b;
+    }
+    __syncthreads();
+
+    const int ntiles = (seg_end - seg + TILE - 1) / TILE;
+    for (int tile = wave; tile < ntiles; tile += kWaves) {
+      const int tbase = seg + tile * TILE;
+      u32x4 kr[U], vr[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = tbase + u * TPL + grp;
+        ok[u] = t < seg_end;
+        if (ok[u]) {
+          const int64_t blk = s_tbl[(t >> lbs) - first_blk];
+          const int64_t off =
+              ((blk * a.num_kv_heads + kvh) << lbs | (t & off_mask)) * row_bytes + lane_bytes;
+          kr[u] = load16(kbase + off);
+          vr[u] = load16(vbase + off);
+        } else {
+          kr[u] = u32x4{0u, 0u, 0u, 0u};
+          vr[u] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+
+      float s[GT][U];
+#pragma unroll
+      for (int h = 0; h < GT; ++h)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float d = group_sum<LPT>(E::dot(q[h], kr[u], 0.f)) * scale_log2;
+          s[h][u] = ok[u] ? d : -__builtin_inff();
+        }
+
+      float vf[U][EPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[u][e] = E::elem(vr[u], e);
+
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        float tmax = s[h][0];
+#pragma unroll
+        for (int u = 1; u < U; ++u) tmax = fmaxf(tmax, s[h][u]);
+        const float m_new = fmaxf(m[h], tmax);
+        const float m_use = safe_max(m_new);
+        const float alpha = exp2_fast(m[h] - m_use);
+        m[h] = m_new;
+        l[h] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float p = exp2_fast(s[h][u] - m_use);
+          l[h] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = __builtin_fmaf(p, vf[u][e], acc[h][e]);
+        }
+      }
+    }
+  }
+
+  // Merge the token streams of this wave (lanes with the same slice).
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    const float mw = across_groups_max<LPT>(m[h]);
+    const float f = exp2_fast(m[h] - safe_max(mw));
+    l[h] = across_groups_sum<LPT>(l[h] * f);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = across_groups_sum<LPT>(acc[h][e] * f);
+    m[h] = mw;
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][h][sub * EPL + e] = acc[h][e];
+      if (lane == 0) {
+        s_max[wave][h] = m[h];
+        s_sum[wave][h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the 4 waves and write the output or this partition's state.
+  for (int idx = tid; idx < nh * D; idx += kDecodeThreads) {
+    const int h = idx / D;
+    const int d = idx - h * D;
+    float mx = s_max[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, s_max[w][h]);
+    const float mu = safe_max(mx);
+    float den = 0.f, num = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = exp2_fast(s_max[w][h] - mu);
+      den = __builtin_fmaf(f, s_sum[w][h], den);
+      num = __builtin_fmaf(f, s_acc[w][h][d], num);
+    }
+    const int64_t row = static_cast<int64_t>(seq) * a.num_heads + h_first + h;
+    if (nparts == 1) {
+      E::store(a.out, row * D + d, den == 0.f ? 0.f : num / den);
+    } else {
+      const int64_t ws = row * a.num_parts + part;
+      a.ws_acc[ws * D + d] = num;
+      if (d == 0) {
+        a.ws_max[ws] = mx;
+        a.ws_sum[ws] = den;
+      }
+    }
+  }
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_reduce_kernel(DecodeArgs a) {
+  constexpr int PER = D / kWave;
+  const int row = blockIdx.x * kWaves + threadIdx.x / kWave;  // seq * Hq + head
+  const int lane = threadIdx.x & (kWave - 1);
+  if (row >= a.num_seqs * a.num_heads) return;
+  const int seq = row / a.num_heads;
+  const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
+  const int nparts = max(1, (ctx + a.part_tokens - 1) / a.part_tokens);
+  if (nparts <= 1) return;  // written by the partition kernel
+  const int64_t base = static_cast<int64_t>(row) * a.num_parts;
+
+  float mx = -__builtin_inff();
+  for (int p = lane; p < nparts; p += kWave) mx = fmaxf(mx, a.ws_max[base + p]);
+  mx = across_groups_max<1>(mx);
+  const float mu = safe_max(mx);
+  float den = 0.f;
+  for (int p = lane; p < nparts; p += kWave) den += exp2_fast(a.ws_max[base + p] - mu) * a.ws_sum[base + p];
+  den = across_groups_sum<1>(den);
+
+  float num[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) num[j] = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float f = exp2_fast(a.ws_max[base + p] - mu);
+    const float* src = a.ws_acc + (base + p) * D + lane * PER;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) num[j] = __builtin_fmaf(f, src[j], num[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    E::store(a.out, static_cast<int64_t>(row) * D + lane * PER + j, den == 0.f ? 0.f : num[j] / den);
+}
+
+template <typename E, int D, int GT>
+hipError_t launch_partitions_gt(const DecodeArgs& a, hipStream_t stream) {
+  const int group = a.num_heads / a.num_kv_heads;
+  const int chunks = (group + GT - 1) / GT;
+  const uint64_t n = static_cast<uint64_t>(a.num_seqs) * a.num_kv_heads * a.num_parts * chunks;
+  if (n == 0) return hipSuccess;
+  const uint32_t per = static_cast<uint32_t>((n + 7) / 8);
+  const float scale_log2 = a.scale * kLog2e;
+  hipLaunchKernelGGL((decode_partition_kernel<E, D, GT>), dim3(per * 8), dim3(kDecodeThreads), 0,
+                     stream, a, chunks, static_cast<uint32_t>(n), per, scale_log2);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t launch_partitions_d(const DecodeArgs& a, hipStream_t stream) {
+  const int group = a.num_heads / a.num_kv_heads;
+  switch (group < kMaxHeadsPerWg ? group : kMaxHeadsPerWg) {
+    case 1: return launch_partitions_gt<E, D, 1>(a, stream);
+    case 2: return launch_partitions_gt<E, D, 2>(a, stream);
+    case 3: return launch_partitions_gt<E, D, 3>(a, stream);
+    case 4: return launch_partitions_gt<E, D, 4>(a, stream);
+    case 5: return launch_partitions_gt<E, D, 5>(a, stream);
+    case 6: return launch_partitions_gt<E, D, 6>(a, stream);
+    case 7: return launch_partitions_gt<E, D, 7>(a, stream);
+    default: return launch_partitions_gt<E, D, 8>(a, stream);
+  }
+}
+
+template <typename E>
+hipError_t launch_partitions_e(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_partitions_d<E, 64>(a, stream);
+    case 128: return launch_partitions_d<E, 128>(a, stream);
+    default: return launch_partitions_d<E, 256>(a, stream);
+  }
+}
+
+template <typename E>
+hipError_t launch_reduce_e(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_heads;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((rows + kWaves - 1) / kWaves));
+  switch (a.head_dim) {
+    case 64: hipLaunchKernelGGL((decode_reduce_kernel<E, 64>), grid, dim3(kDecodeThreads), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((decode_reduce_kernel<E, 128>), grid, dim3(kDecodeThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_reduce_kernel<E, 256>), grid, dim3(kDecodeThreads), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+DecodeWorkspace decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t num_parts) {
+  DecodeWorkspace w{};
+  if (num_parts <= 1 || num_seqs <= 0) return w;
+  const size_t n = static_cast<size_t>(num_seqs) * num_heads * num_parts;
+  w.off_max = 0;
+  w.off_sum = align256(n * sizeof(float));
+  w.off_acc = w.off_sum + align256(n * sizeof(float));
+  w.bytes = w.off_acc + align256(n * head_dim * sizeof(float));
+  return w;
+}
+
+hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.dtype) {
+    case PA_DTYPE_F32: return launch_partitions_e<F32>(a, stream);
+    case PA_DTYPE_F16: return launch_partitions_e<F16>(a, stream);
+    default: return launch_partitions_e<BF16>(a, stream);
+  }
+}
+
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_parts <= 1) return hipSuccess;
+  switch (a.dtype) {
+    case PA_DTYPE_F32: return launch_reduce_e<F32>(a, stream);
+    case PA_DTYPE_F16: return launch_reduce_e<F16>(a, stream);
+    default: return launch_reduce_e<BF16>(a, stream);
+  }
+}
+
+}  // namespace pa

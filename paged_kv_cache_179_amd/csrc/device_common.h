@@ -1,0 +1,133 @@
+// Device-side helpers shared by the gfx950 kernels of this library:
+// element-type traits for 16-byte register groups, wavefront reductions built
+// on DPP row operations, and small math wrappers over the hardware
+// instructions.  wave64 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// Element types.  A "group" is the 16 bytes one lane moves per load.
+// ---------------------------------------------------------------------------
+struct F32 {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerGroup = 4;
+  __device__ static inline float elem(const u32x4& g, int e) { return __uint_as_float(g[e]); }
+  // sum_e q[e] * k[e] + acc over one group
+  __device__ static inline float dot(const u32x4& q, const u32x4& k, float acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_fmaf(__uint_as_float(q[e]), __uint_as_float(k[e]), acc);
+    return acc;
+  }
+  __device__ static inline void store(void* base, int64_t idx, float v) {
+    static_cast<float*>(base)[idx] = v;
+  }
+};
+
+struct F16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerGroup = 8;
+  __device__ static inline float elem(const u32x4& g, int e) {
+    // A vector subscript is copied to a scalar before __builtin_bit_cast: bit-casting
+    // the subscript expression itself reads element 0 with this compiler.
+    const unsigned w = g[e >> 1];
+    const f16x2 h = __builtin_bit_cast(f16x2, w);
+    return static_cast<float>(h[e & 1]);
+  }
+  __device__ static inline float dot(const u32x4& q, const u32x4& k, float acc) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const unsigned qw = q[w], kw = k[w];
+      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qw), __builtin_bit_cast(f16x2, kw), acc,
+                                   false);
+    }
+    return acc;
+  }
+  __device__ static inline void store(void* base, int64_t idx, float v) {
+    static_cast<_Float16*>(base)[idx] = static_cast<_Float16>(v);
+  }
+};
+
+struct BF16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerGroup = 8;
+  __device__ static inline float elem(const u32x4& g, int e) {
+    const unsigned w = g[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+  __device__ static inline float dot(const u32x4& q, const u32x4& k, float acc) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const unsigned qw = q[w], kw = k[w];
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw),
+                                            __builtin_bit_cast(bf16x2, kw), acc, false);
+    }
+    return acc;
+  }
+  __device__ static inline void store(void* base, int64_t idx, float v) {
+    static_cast<__bf16*>(base)[idx] = static_cast<__bf16>(v);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers.
+// ---------------------------------------------------------------------------
+template <int kCtrl>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes (N = 1, 2, 4, ..., 64); every lane of a
+// group ends with the group's sum.  Within a 16-lane row the exchanges are
+// DPP quad permutes and row mirrors; wider groups use a swizzle (xor 16) and
+// a cross-half exchange (xor 32).
+template <int N>
+__device__ inline float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror
+  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror
+  if constexpr (N >= 32)
+    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // xor 16
+  if constexpr (N >= 64) x += __shfl_xor(x, 32, kWave);
+  return x;
+}
+
+// Max / sum across groups: lanes l, l ^ N, l ^ 2N, ... (N = group width).
+template <int N>
+__device__ inline float across_groups_max(float x) {
+#pragma unroll
+  for (int off = N; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+template <int N>
+__device__ inline float across_groups_sum(float x) {
+#pragma unroll
+  for (int off = N; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Offset used to exponentiate scores against a running max that may still be
+// -inf (no finite score seen yet): then every exponent is -inf and gives 0.
+__device__ inline float safe_max(float m) { return m == -__builtin_inff() ? 0.f : m; }
+
+__device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
+
+// Workgroup index -> logical work index such that each of the 8 XCDs (which
+// receive workgroups round-robin) processes one contiguous range of the
+// logical order.  `per` = ceil(n / 8); the grid has 8 * per workgroups.
+__device__ inline uint32_t xcd_remap(uint32_t b, uint32_t per) { return (b & 7u) * per + (b >> 3); }
+
+}  // namespace pa

@@ -1,0 +1,303 @@
+// C-ABI entry points: argument validation, workspace sizing and dispatch to the
+// gfx950 kernels.  Validation happens entirely on the host and before any HIP
+// call, so every error path returns a status with nothing enqueued.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "paged_attention.h"
+#include "pa_internal.h"
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int log2i(int64_t x) {
+  int r = 0;
+  while ((int64_t(1) << r) < x) ++r;
+  return r;
+}
+
+bool supported_dtype(int d) { return d == PA_DTYPE_F32 || d == PA_DTYPE_F16 || d == PA_DTYPE_BF16; }
+bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256; }
+bool supported_block_size(int b) { return is_pow2(b) && b <= 256; }
+int elem_bytes(int d) { return d == PA_DTYPE_F32 ? 4 : 2; }
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int32_t clamp_i32(int64_t v) {
+  return static_cast<int32_t>(std::min<int64_t>(std::max<int64_t>(v, 0), INT32_MAX));
+}
+
+// Decode geometry shared by the sizing function and both decode halves.
+struct DecodeGeom {
+  int32_t ctx_limit;
+  int32_t part_tokens;
+  int32_t num_parts;
+};
+
+DecodeGeom decode_geom(int64_t ctx_limit, int32_t partition_size) {
+  DecodeGeom g{};
+  g.ctx_limit = clamp_i32(ctx_limit);
+  g.part_tokens = partition_size > 0 ? partition_size : std::max<int32_t>(g.ctx_limit, 1);
+  g.num_parts = std::max<int32_t>(
+      1, static_cast<int32_t>((static_cast<int64_t>(g.ctx_limit) + g.part_tokens - 1) / g.part_tokens));
+  return g;
+}
+
+pa_status check_decode_shapes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int32_t num_blocks, int32_t max_context_len, int32_t partition_size,
+                              int dtype) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      max_context_len < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 0 && (max_blocks_per_seq <= 0 || num_blocks <= 0)) return PA_ERR_BAD_SHAPE;
+  if (partition_size < 0 || (partition_size > 0 && (partition_size % 64 != 0 ||
+                                                     partition_size % block_size != 0)))
+    return PA_ERR_BAD_SHAPE;
+  return PA_OK;
+}
+
+pa_status check_workspace(size_t needed, const void* workspace, size_t workspace_bytes) {
+  if (needed == 0) return PA_OK;
+  if (workspace == nullptr) return PA_ERR_NULL_POINTER;
+  if (workspace_bytes < needed) return PA_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(workspace, 16)) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+pa_status decode_args(void* out, const void* query, const void* key_cache, const void* value_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int32_t num_blocks, int32_t max_context_len, float scale,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes,
+                      pa_dtype dtype, pa::DecodeArgs* a) {
+  pa_status st = check_decode_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                     max_blocks_per_seq, num_blocks, max_context_len,
+                                     partition_size, dtype);
+  if (st != PA_OK || num_seqs == 0) return st;
+  if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return PA_ERR_UNSUPPORTED;
+  const DecodeGeom g = decode_geom(
+      std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size),
+      partition_size);
+  const pa::DecodeWorkspace w =
+      pa::decode_workspace_layout(num_seqs, num_heads, head_dim, g.num_parts);
+  st = check_workspace(w.bytes, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  *a = pa::DecodeArgs{};
+  a->out = out;
+  a->query = query;
+  a->key_cache = key_cache;
+  a->value_cache = value_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->ws_max = w.bytes ? reinterpret_cast<float*>(ws + w.off_max) : nullptr;
+  a->ws_sum = w.bytes ? reinterpret_cast<float*>(ws + w.off_sum) : nullptr;
+  a->ws_acc = w.bytes ? reinterpret_cast<float*>(ws + w.off_acc) : nullptr;
+  a->num_seqs = num_seqs;
+  a->num_heads = num_heads;
+  a->num_kv_heads = num_kv_heads;
+  a->head_dim = head_dim;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->log2_block_size = log2i(block_size);
+  a->num_blocks = num_blocks;
+  a->ctx_limit = g.ctx_limit;
+  a->part_tokens = g.part_tokens;
+  a->num_parts = g.num_parts;
+  a->scale = scale;
+  a->dtype = dtype;
+  return PA_OK;
+}
+
+pa_status to_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL_POINTER: return "null pointer argument";
+    case PA_ERR_BAD_SHAPE: return "inconsistent or negative size argument";
+    case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, block_size or alignment";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int pa_version(void) { return 100; }
+
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
+                               void* value_cache, const int64_t* slot_mapping,
+                               int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                               void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return PA_ERR_BAD_SHAPE;
+  if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(slot_mapping, 8))
+    return PA_ERR_UNSUPPORTED;
+  pa::CacheWriteArgs a{key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                       num_kv_heads, head_dim, log2i(block_size), num_blocks, elem_bytes(dtype)};
+  return to_status(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || partition_size < 0) return 0;
+  const DecodeGeom g = decode_geom(max_context_len, partition_size);
+  return pa::decode_workspace_layout(num_seqs, num_heads, head_dim, g.num_parts).bytes;
+}
+
+pa_status pa_decode_partitions(void* out, const void* query, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               int32_t max_context_len, float scale, int32_t partition_size,
+                               void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                               void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                             context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, max_context_len, scale, partition_size,
+                             workspace, workspace_bytes, dtype, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  return to_status(pa::launch_decode_partitions(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                           int32_t block_size, int32_t max_context_len, int32_t partition_size,
+                           const void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                           void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0) return PA_ERR_BAD_SHAPE;
+  if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_seqs > 0 && max_blocks_per_seq <= 0) return PA_ERR_BAD_SHAPE;
+  if (partition_size < 0 || (partition_size > 0 && (partition_size % 64 != 0 ||
+                                                     partition_size % block_size != 0)))
+    return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !context_lens) return PA_ERR_NULL_POINTER;
+  if (!aligned(out, 16) || !aligned(context_lens, 4)) return PA_ERR_UNSUPPORTED;
+  const DecodeGeom g = decode_geom(
+      std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size),
+      partition_size);
+  const pa::DecodeWorkspace w = pa::decode_workspace_layout(num_seqs, num_heads, head_dim, g.num_parts);
+  pa_status st = check_workspace(w.bytes, workspace, workspace_bytes);
+  if (st != PA_OK || w.bytes == 0) return st;
+  pa::DecodeArgs a{};
+  const char* ws = static_cast<const char*>(workspace);
+  a.out = out;
+  a.context_lens = context_lens;
+  a.ws_max = reinterpret_cast<float*>(const_cast<char*>(ws) + w.off_max);
+  a.ws_sum = reinterpret_cast<float*>(const_cast<char*>(ws) + w.off_sum);
+  a.ws_acc = reinterpret_cast<float*>(const_cast<char*>(ws) + w.off_acc);
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.ctx_limit = g.ctx_limit;
+  a.part_tokens = g.part_tokens;
+  a.num_parts = g.num_parts;
+  a.dtype = dtype;
+  return to_status(pa::launch_decode_reduce(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_decode(void* out, const void* query, const void* key_cache, const void* value_cache,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, int32_t max_context_len, float scale,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    pa_dtype dtype, void* stream) {
+  pa::DecodeArgs a;
+  pa_status st = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                             context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, max_context_len, scale, partition_size,
+                             workspace, workspace_bytes, dtype, &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = to_status(pa::launch_decode_partitions(a, s));
+  if (st != PA_OK) return st;
+  return to_status(pa::launch_decode_reduce(a, s));
+}
+
+size_t pa_prefill_workspace_bytes(int32_t num_q_tokens, int32_t num_seqs, int32_t num_heads,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
+                                  int32_t max_context_len) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_query_len;
+  if (num_q_tokens <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  return pa::prefill_workspace_layout(num_q_tokens, num_heads, head_dim,
+                                      pa::prefill_num_splits(max_context_len))
+      .bytes;
+}
+
+pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_start_loc,
+                           int32_t num_q_tokens, int32_t max_query_len, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_context_len, float scale, void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  if (num_q_tokens < 0 || max_query_len < 0) return PA_ERR_BAD_SHAPE;
+  pa_status st = check_decode_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                     max_blocks_per_seq, num_blocks, max_context_len, 0, dtype);
+  if (st != PA_OK) return st;
+  if (dtype == PA_DTYPE_F32 || num_heads / num_kv_heads > 128) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_q_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !query || !query_start_loc || !key_cache || !value_cache || !block_tables ||
+      !context_lens)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(query_start_loc, 4))
+    return PA_ERR_UNSUPPORTED;
+  const int32_t ctx_limit = clamp_i32(
+      std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size));
+  if (ctx_limit == 0) return PA_OK;
+  const pa::PrefillWorkspace w = pa::prefill_workspace_layout(
+      num_q_tokens, num_heads, head_dim, pa::prefill_num_splits(ctx_limit));
+  st = check_workspace(w.bytes, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.query = query;
+  a.query_start_loc = query_start_loc;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_q_tokens = num_q_tokens;
+  a.max_query_len = max_query_len;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.log2_block_size = log2i(block_size);
+  a.num_blocks = num_blocks;
+  a.ctx_limit = ctx_limit;
+  a.scale = scale;
+  a.dtype = dtype;
+  return to_status(pa::launch_prefill(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,96 @@
+// Host-side interface between the C-ABI shim (pa_api.cpp) and the kernel
+// translation units.  Every argument here has already been validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "paged_attention.h"
+
+namespace pa {
+
+constexpr int kDecodeThreads = 256;  // 4 waves per decode workgroup
+constexpr int kSegTokens = 512;      // tokens whose block ids are staged in LDS at once
+constexpr int kMaxHeadsPerWg = 8;    // query heads of one KV head handled by one workgroup
+
+struct CacheWriteArgs {
+  const void* key;
+  const void* value;
+  void* key_cache;
+  void* value_cache;
+  const int64_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t log2_block_size;
+  int32_t num_blocks;
+  int32_t elem_bytes;
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* query;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  float* ws_max;   // [S][Hq][P] running max (log2 units)
+  float* ws_sum;   // [S][Hq][P] softmax denominators
+  float* ws_acc;   // [S][Hq][P][D] un-normalised partial outputs
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t log2_block_size;
+  int32_t num_blocks;
+  int32_t ctx_limit;       // min(max_context_len, max_blocks_per_seq * block_size)
+  int32_t part_tokens;     // tokens per partition (> 0)
+  int32_t num_parts;       // partitions covering ctx_limit
+  float scale;
+  pa_dtype dtype;
+};
+
+struct DecodeWorkspace {
+  size_t bytes;
+  size_t off_max, off_sum, off_acc;
+};
+DecodeWorkspace decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                        int32_t num_parts);
+
+struct PrefillArgs {
+  void* out;
+  const void* query;
+  const int32_t* query_start_loc;
+  const void* key_cache;
+  const void* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_q_tokens;
+  int32_t max_query_len;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t max_blocks_per_seq;
+  int32_t log2_block_size;
+  int32_t num_blocks;
+  int32_t ctx_limit;
+  float scale;
+  pa_dtype dtype;
+};
+
+hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);
+hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
+struct PrefillWorkspace {
+  size_t bytes;
+  size_t off_max, off_sum, off_acc;
+};
+int32_t prefill_num_splits(int32_t ctx_limit);
+PrefillWorkspace prefill_workspace_layout(int32_t num_q_tokens, int32_t num_heads,
+                                          int32_t head_dim, int32_t nsplit);
+hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,77 @@
+"""Test utilities: dtype conversions and running the oracle on a workload.
+
+Nothing here computes attention; the oracle does (``oracle/``), and the HIP
+library does through the binding.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+TOL = {"fp32": 1e-5, "fp16": 1e-2, "bf16": 1e-2}
+RAW = {torch.float32: torch.int32, torch.float16: torch.int16, torch.bfloat16: torch.int16}
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a (CPU or GPU) tensor."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def raw(t: torch.Tensor) -> np.ndarray:
+    """Bit pattern of a tensor as a numpy integer array."""
+    return t.detach().to("cpu").contiguous().view(RAW[t.dtype]).numpy()
+
+
+def written_caches(w):
+    """Caches after the step's cache write, computed by the oracle (raw bits)."""
+    kc, vc = oracle.reshape_and_cache(raw(w.new_key), raw(w.new_value), raw(w.key_cache),
+                                      raw(w.value_cache), w.slot_mapping, w.block_size)
+    dt = w.torch_dtype
+    return (torch.from_numpy(kc).view(dt), torch.from_numpy(vc).view(dt))
+
+
+def oracle_decode(w, kc, vc, rows=None):
+    """Oracle decode output for the decode rows (optionally a subset of them)."""
+    idx = np.arange(len(w.decode_rows)) if rows is None else np.asarray(rows)
+    seqs = w.decode_rows[idx]
+    return oracle.paged_decode(f64(w.query_decode)[idx], f64(kc), f64(vc), w.block_tables[seqs],
+                               w.context_lens[seqs], w.scale, w.block_size)
+
+
+def oracle_prefill(w, kc, vc):
+    seqs = w.prefill_rows
+    return oracle.paged_prefill_chunk(f64(w.query_prefill), w.query_start_loc, f64(kc), f64(vc),
+                                      w.block_tables[seqs], w.context_lens[seqs], w.scale,
+                                      w.block_size)
+
+
+def to_dev(w, device):
+    """Device copies of every input of a workload."""
+    d = {}
+    d["key_cache"] = w.key_cache.to(device)
+    d["value_cache"] = w.value_cache.to(device)
+    d["new_key"] = w.new_key.to(device)
+    d["new_value"] = w.new_value.to(device)
+    d["slot_mapping"] = torch.from_numpy(w.slot_mapping).to(device)
+    bt = torch.from_numpy(w.block_tables)
+    cl = torch.from_numpy(w.context_lens)
+    dr = torch.from_numpy(w.decode_rows)
+    pr = torch.from_numpy(w.prefill_rows)
+    d["bt_decode"] = bt[dr].contiguous().to(device)
+    d["cl_decode"] = cl[dr].contiguous().to(device)
+    d["bt_prefill"] = bt[pr].contiguous().to(device)
+    d["cl_prefill"] = cl[pr].contiguous().to(device)
+    d["query_decode"] = w.query_decode.to(device)
+    d["query_prefill"] = w.query_prefill.to(device)
+    d["qsl"] = torch.from_numpy(w.query_start_loc).to(device)
+    return d
+
+
+def max_err(gpu_out: torch.Tensor, ref: np.ndarray) -> float:
+    g = f64(gpu_out)
+    if g.size == 0:
+        return 0.0
+    assert np.isfinite(g).all(), "non-finite GPU output"
+    return float(np.max(np.abs(g - ref)))

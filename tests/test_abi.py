@@ -1,0 +1,147 @@
+"""The C ABI loads, exports every declared symbol, and rejects bad arguments
+on the host (CPU only: every call here fails validation, so nothing is ever
+launched)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from paged_kv_cache_179_amd import binding
+
+# The validation tests pass placeholder device pointers that must never reach
+# a kernel; keep them off machines where a launch could actually happen.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="host-validation tests use placeholder pointers")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+OK, NULLP, SHAPE, UNSUP, WS, LAUNCH = 0, 1, 2, 3, 4, 5
+F32, F16, BF16 = 0, 1, 2
+P = ctypes.c_void_p(1 << 20)  # non-null, 256-aligned; never dereferenced (validation fails first)
+N = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not binding.library_path().exists():
+        from paged_kv_cache_179_amd.build import build
+
+        build()
+    return binding.library()
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(HEADER_DIR)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w \*]*?\b(pa_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"pa_reshape_and_cache", "pa_decode", "pa_prefill_chunk"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(binding.EXPORTED) == set(names), "binding and header disagree"
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.pa_status_str(s) and lib.pa_status_str(s) != b"unknown status"
+    assert lib.pa_status_str(99) == b"unknown status"
+    assert lib.pa_version() >= 100
+
+
+def write(lib, key=P, value=P, kc=P, vc=P, slots=P, n=4, hkv=2, d=64, bs=16, nb=8, dt=BF16):
+    return lib.pa_reshape_and_cache(key, value, kc, vc, slots, n, hkv, d, bs, nb, dt, N)
+
+
+def test_write_validation(lib):
+    assert write(lib, n=-1) == SHAPE
+    assert write(lib, hkv=0) == SHAPE
+    assert write(lib, d=96) == UNSUP
+    assert write(lib, bs=3) == UNSUP
+    assert write(lib, bs=512) == UNSUP
+    assert write(lib, dt=7) == UNSUP
+    assert write(lib, key=N) == NULLP
+    assert write(lib, slots=N) == NULLP
+    assert write(lib, kc=ctypes.c_void_p((1 << 20) + 8)) == UNSUP  # misaligned
+    assert write(lib, n=0, key=N, value=N, kc=N, vc=N, slots=N) == OK  # empty is a no-op
+
+
+def decode(lib, fn="pa_decode", out=P, q=P, kc=P, vc=P, bt=P, mbps=100, cl=P, s=4, hq=8, hkv=2,
+           d=128, bs=16, nb=64, maxc=1000, scale=0.1, part=512, ws=P, wsb=1 << 30, dt=F16):
+    return getattr(lib, fn)(out, q, kc, vc, bt, mbps, cl, s, hq, hkv, d, bs, nb, maxc, scale, part,
+                            ws, wsb, dt, N)
+
+
+@pytest.mark.parametrize("fn", ["pa_decode", "pa_decode_partitions"])
+def test_decode_validation(lib, fn):
+    assert decode(lib, fn, hkv=3) == SHAPE           # 8 % 3 != 0
+    assert decode(lib, fn, s=-1) == SHAPE
+    assert decode(lib, fn, maxc=-5) == SHAPE
+    assert decode(lib, fn, d=80) == UNSUP
+    assert decode(lib, fn, bs=24) == UNSUP
+    assert decode(lib, fn, dt=3) == UNSUP
+    assert decode(lib, fn, part=100) == SHAPE        # not a multiple of 64
+    assert decode(lib, fn, part=64, bs=128) == SHAPE  # not a multiple of block_size
+    assert decode(lib, fn, mbps=0) == SHAPE
+    assert decode(lib, fn, nb=0) == SHAPE
+    assert decode(lib, fn, out=N) == NULLP
+    assert decode(lib, fn, cl=N) == NULLP
+    assert decode(lib, fn, q=ctypes.c_void_p((1 << 20) + 4)) == UNSUP
+    assert decode(lib, fn, ws=N) == NULLP            # 2 partitions need a workspace
+    need = lib.pa_decode_workspace_bytes(4, 8, 128, 1000, 512)
+    assert need > 0
+    assert decode(lib, fn, wsb=need - 1) == WS
+    assert decode(lib, fn, s=0, out=N, q=N, kc=N, vc=N, bt=N, cl=N) == OK
+
+
+def test_reduce_validation(lib):
+    r = lib.pa_decode_reduce
+    # mbps 100 x block 16 >= 1000 tokens: two partitions, so a workspace is needed.
+    assert r(P, P, 4, 8, 128, 100, 16, 1000, 512, N, 0, F16, N) == NULLP
+    assert r(P, P, 4, 8, 128, 100, 16, 1000, 512, P, 10, F16, N) == WS
+    assert r(P, P, 4, 8, 96, 100, 16, 1000, 512, P, 1 << 30, F16, N) == UNSUP
+    assert r(N, P, 4, 8, 128, 100, 16, 1000, 512, P, 1 << 30, F16, N) == NULLP
+    assert r(P, P, 4, 8, 128, 100, 16, 1000, 100, P, 1 << 30, F16, N) == SHAPE
+
+
+def test_workspace_sizes(lib):
+    f = lib.pa_decode_workspace_bytes
+    assert f(128, 32, 128, 4096, 0) == 0        # never split
+    assert f(128, 32, 128, 512, 512) == 0       # always one partition
+    n = 128 * 32 * 8
+    expect = 2 * ((n * 4 + 255) // 256 * 256) + (n * 128 * 4 + 255) // 256 * 256
+    assert f(128, 32, 128, 4096, 512) == expect
+    assert f(0, 32, 128, 4096, 512) == 0
+    g = lib.pa_prefill_workspace_bytes
+    assert g(2048, 4, 8, 1, 256, 512, 1024) == 0  # one key range
+    assert g(2048, 4, 8, 1, 256, 512, 4096) > 0
+
+
+def prefill(lib, out=P, q=P, qsl=P, nq=64, maxq=32, kc=P, vc=P, bt=P, mbps=8, cl=P, s=2, hq=8,
+            hkv=1, d=256, bs=16, nb=64, maxc=100, scale=0.1, ws=P, wsb=1 << 30, dt=BF16):
+    return lib.pa_prefill_chunk(out, q, qsl, nq, maxq, kc, vc, bt, mbps, cl, s, hq, hkv, d, bs, nb,
+                                maxc, scale, ws, wsb, dt, N)
+
+
+def test_prefill_validation(lib):
+    assert prefill(lib, dt=F32) == UNSUP
+    assert prefill(lib, hq=256, hkv=1) == UNSUP     # group larger than a tile
+    assert prefill(lib, nq=-1) == SHAPE
+    assert prefill(lib, hkv=3) == SHAPE
+    assert prefill(lib, d=32) == UNSUP
+    assert prefill(lib, qsl=N) == NULLP
+    assert prefill(lib, out=N) == NULLP
+    assert prefill(lib, maxc=5000, mbps=400, ws=N) == NULLP
+    assert prefill(lib, maxc=5000, mbps=400, wsb=16) == WS
+    assert prefill(lib, nq=0, out=N, q=N, qsl=N) == OK

@@ -1,0 +1,279 @@
+"""GPU parity: the HIP library against the fp64 oracle on the same seeded inputs.
+
+Cache writes must be bit-exact over the whole pool; attention outputs must be
+within 1e-5 (fp32) or 1e-2 (fp16/bf16, fp32 accumulation) of the oracle.
+Small cases span several tiles, partitions and a ragged tail; the five named
+workloads run at full size in the launch configuration the benchmark times,
+compared on sampled rows.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_179_amd as pa
+from paged_kv_cache_179_amd import workloads as W
+from tests.helpers import (TOL, f64, max_err, oracle_decode, oracle_prefill, raw, to_dev,
+                           written_caches)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_write(w, d):
+    pa.reshape_and_cache(d["new_key"], d["new_value"], d["key_cache"], d["value_cache"],
+                         d["slot_mapping"])
+
+
+def run_decode(w, d, partition_size=512, fn=pa.decode):
+    out = torch.full_like(d["query_decode"], float("nan"))
+    if len(w.decode_rows):
+        maxc = int(w.context_lens[w.decode_rows].max())
+        fn(out, d["query_decode"], d["key_cache"], d["value_cache"], d["bt_decode"],
+           d["cl_decode"], w.scale, maxc, partition_size=partition_size)
+    return out
+
+
+def run_prefill(w, d):
+    out = torch.full_like(d["query_prefill"], float("nan"))
+    if len(w.prefill_rows):
+        lens = np.diff(w.query_start_loc)
+        pa.prefill_chunk(out, d["query_prefill"], d["qsl"], d["key_cache"], d["value_cache"],
+                         d["bt_prefill"], d["cl_prefill"], w.scale, int(lens.max()),
+                         int(w.context_lens[w.prefill_rows].max()))
+    return out
+
+
+SMALL = [
+    # dtype, Hq, Hkv, D, bs
+    ("fp32", 4, 2, 64, 16),
+    ("fp32", 8, 8, 128, 16),
+    ("fp32", 8, 1, 256, 16),
+    ("bf16", 32, 4, 64, 16),
+    ("fp16", 8, 8, 128, 16),
+    ("bf16", 28, 4, 128, 16),
+    ("bf16", 8, 1, 256, 16),
+    ("fp16", 6, 2, 128, 1),
+    ("bf16", 12, 4, 64, 32),
+    ("bf16", 20, 5, 128, 16),
+    ("fp16", 32, 2, 128, 16),   # group 16: two head chunks per KV head
+    ("bf16", 5, 1, 64, 256),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[0]}-h{c[1]}x{c[2]}-d{c[3]}-bs{c[4]}" for c in SMALL])
+@pytest.mark.parametrize("partition_size", [512, 0, 64])
+def test_decode_small(gpu, case, partition_size):
+    dtype, hq, hkv, d_, bs = case
+    if partition_size and partition_size % bs:
+        pytest.skip("partition must be a multiple of the block size")
+    say(f"decode small {case} part={partition_size}")
+    w = W.small_case(100 + hq + d_ + bs, num_seqs=7, ctx_lo=1, ctx_hi=1300, num_heads=hq,
+                     num_kv_heads=hkv, head_dim=d_, block_size=bs, dtype=dtype,
+                     extra_ctx=[1, 2, 512, 513, 1025])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    out = run_decode(w, d, partition_size)
+    torch.cuda.synchronize()
+    kc, vc = written_caches(w)
+    err = max_err(out, oracle_decode(w, kc, vc))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_cache_write_bit_exact(gpu, dtype):
+    w = W.small_case(7, num_seqs=9, ctx_lo=1, ctx_hi=200, num_heads=8, num_kv_heads=4,
+                     head_dim=128, block_size=16, dtype=dtype, chunk_lens=[37, 5])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    torch.cuda.synchronize()
+    kc, vc = written_caches(w)
+    assert np.array_equal(raw(d["key_cache"]), raw(kc))
+    assert np.array_equal(raw(d["value_cache"]), raw(vc))
+
+
+def test_cache_write_skips_negative_and_out_of_pool_slots(gpu):
+    w = W.small_case(8, num_seqs=4, ctx_lo=10, ctx_hi=40, num_heads=2, num_kv_heads=2,
+                     head_dim=64, block_size=16, dtype="bf16")
+    slots = w.slot_mapping.copy()
+    slots[1] = -1
+    slots[2] = w.num_blocks * w.block_size  # one past the pool
+    w.slot_mapping = slots
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    torch.cuda.synchronize()
+    import oracle
+
+    kc, _ = oracle.reshape_and_cache(raw(w.new_key), raw(w.new_value), raw(w.key_cache),
+                                     raw(w.value_cache), np.where(slots >= w.num_blocks * 16, -1, slots),
+                                     w.block_size)
+    assert np.array_equal(raw(d["key_cache"]), kc)
+
+
+@pytest.mark.parametrize("case", [("bf16", 8, 1, 256, 16), ("fp16", 16, 4, 128, 16),
+                                  ("bf16", 28, 4, 128, 16), ("fp16", 4, 4, 64, 16),
+                                  ("bf16", 14, 2, 64, 1), ("fp16", 8, 2, 128, 32)],
+                         ids=lambda c: f"{c[0]}-h{c[1]}x{c[2]}-d{c[3]}-bs{c[4]}")
+def test_prefill_small(gpu, case):
+    dtype, hq, hkv, d_, bs = case
+    say(f"prefill small {case}")
+    # chunks with prior context 0, short, across a key-range boundary, and L = 1
+    w = W.small_case(200 + hq + d_, num_seqs=6, ctx_lo=1, ctx_hi=600, num_heads=hq,
+                     num_kv_heads=hkv, head_dim=d_, block_size=bs, dtype=dtype,
+                     chunk_lens=[70, 33, 130, 1, 64], extra_ctx=[70, 100, 1400, 900, 2100])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    out = run_prefill(w, d)
+    dec = run_decode(w, d)
+    torch.cuda.synchronize()
+    kc, vc = written_caches(w)
+    err = max_err(out, oracle_prefill(w, kc, vc))
+    say(f"  prefill max abs err {err:.3e}")
+    assert err <= TOL[dtype]
+    assert max_err(dec, oracle_decode(w, kc, vc)) <= TOL[dtype]
+
+
+def test_prefill_single_token_rows_match_decode(gpu):
+    w = W.small_case(31, num_seqs=6, ctx_lo=1, ctx_hi=3000, num_heads=8, num_kv_heads=2,
+                     head_dim=128, block_size=16, dtype="bf16", extra_ctx=[1, 1024, 1025])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    dec = run_decode(w, d)
+    qsl = torch.arange(w.num_seqs + 1, dtype=torch.int32, device=gpu)
+    pre = torch.empty_like(dec)
+    pa.prefill_chunk(pre, d["query_decode"], qsl, d["key_cache"], d["value_cache"], d["bt_decode"],
+                     d["cl_decode"], w.scale, 1, int(w.context_lens.max()))
+    torch.cuda.synchronize()
+    assert float((pre.float() - dec.float()).abs().max()) <= 1e-2
+    kc, vc = written_caches(w)
+    assert max_err(pre, oracle_decode(w, kc, vc)) <= 1e-2
+
+
+def test_partition_size_does_not_change_result(gpu):
+    w = W.small_case(41, num_seqs=5, ctx_lo=1, ctx_hi=4000, num_heads=4, num_kv_heads=2,
+                     head_dim=64, block_size=16, dtype="fp32", extra_ctx=[4000, 1, 511])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    outs = {p: run_decode(w, d, p) for p in (0, 64, 256, 512, 1024)}
+    torch.cuda.synchronize()
+    for p, o in outs.items():
+        assert float((o - outs[0]).abs().max()) <= 1e-6, p
+    kc, vc = written_caches(w)
+    assert max_err(outs[512], oracle_decode(w, kc, vc)) <= 1e-5
+
+
+def test_decode_halves_equal_decode(gpu):
+    w = W.small_case(51, num_seqs=6, ctx_lo=1, ctx_hi=2500, num_heads=8, num_kv_heads=2,
+                     head_dim=128, block_size=16, dtype="fp16")
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    full = run_decode(w, d)
+    half = torch.full_like(full, float("nan"))
+    maxc = int(w.context_lens.max())
+    ws = pa.decode_partitions(half, d["query_decode"], d["key_cache"], d["value_cache"],
+                              d["bt_decode"], d["cl_decode"], w.scale, maxc, partition_size=512)
+    pa.decode_reduce(half, d["cl_decode"], 8, 128, w.max_blocks_per_seq, 16, maxc, 512, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(full, half)
+
+
+def test_batch_equals_single_sequence_launches(gpu):
+    w = W.small_case(61, num_seqs=5, ctx_lo=1, ctx_hi=1500, num_heads=28, num_kv_heads=4,
+                     head_dim=128, block_size=16, dtype="bf16")
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    full = run_decode(w, d)
+    for s in range(w.num_seqs):
+        one = torch.empty_like(full[s:s + 1])
+        pa.decode(one, d["query_decode"][s:s + 1].contiguous(), d["key_cache"], d["value_cache"],
+                  d["bt_decode"][s:s + 1].contiguous(), d["cl_decode"][s:s + 1].contiguous(),
+                  w.scale, int(w.context_lens[s]), partition_size=512)
+        torch.cuda.synchronize()
+        assert torch.equal(one[0], full[s])
+
+
+def test_empty_context_gives_zeros(gpu):
+    w = W.small_case(71, num_seqs=3, ctx_lo=5, ctx_hi=50, num_heads=4, num_kv_heads=2,
+                     head_dim=64, block_size=16, dtype="bf16")
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    d["cl_decode"][1] = 0
+    out = run_decode(w, d)
+    torch.cuda.synchronize()
+    assert torch.all(out[1] == 0)
+    assert torch.isfinite(out).all()
+
+
+def test_missing_write_is_loud(gpu):
+    w = W.small_case(81, num_seqs=3, ctx_lo=5, ctx_hi=50, num_heads=4, num_kv_heads=2,
+                     head_dim=64, block_size=16, dtype="bf16")
+    d = to_dev(w, gpu)
+    out = run_decode(w, d)  # no cache write: the current token's slot is NaN
+    torch.cuda.synchronize()
+    assert torch.isnan(out).all()
+
+
+def test_tiny_full(gpu):
+    w = W.make("tiny")
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    out = run_decode(w, d, w.partition_size)
+    torch.cuda.synchronize()
+    kc, vc = written_caches(w)
+    assert np.array_equal(raw(d["key_cache"]), raw(kc))
+    ref = oracle_decode(w, kc, vc)
+    err = max_err(out, ref)
+    say(f"tiny max abs err {err:.3e}")
+    assert err <= 1e-5
+    # context 1: the output is the new token's value row (bit for bit after rounding)
+    g = w.num_heads // w.num_kv_heads
+    for h in range(w.num_heads):
+        assert torch.equal(out[0, h].cpu(), w.new_value[0, h // g])
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["tinyllama", "llama2_7b", "qwen25_7b", "gemma_2b_mixed"])
+def test_full_workload_sampled(gpu, name):
+    say(f"full workload {name}: generating")
+    w = W.make(name)
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    out = run_decode(w, d, w.partition_size)
+    pre = run_prefill(w, d)
+    torch.cuda.synchronize()
+    say(f"full workload {name}: checking")
+    # cache write: the written slots, and a sample of the rest of the pool
+    bs = w.block_size
+    blk = torch.from_numpy(w.slot_mapping // bs)
+    off = torch.from_numpy(w.slot_mapping % bs)
+    got_k = d["key_cache"][blk.to(gpu), :, off.to(gpu), :].cpu()
+    assert torch.equal(got_k.view(torch.int16), w.new_key.view(torch.int16))
+    got_v = d["value_cache"][blk.to(gpu), :, off.to(gpu), :].cpu()
+    assert torch.equal(got_v.view(torch.int16), w.new_value.view(torch.int16))
+    untouched = np.setdiff1d(np.arange(w.num_blocks), np.unique(w.slot_mapping // bs))[:64]
+    assert torch.equal(d["key_cache"][torch.from_numpy(untouched).to(gpu)].cpu().view(torch.int16),
+                       w.key_cache[torch.from_numpy(untouched)].view(torch.int16))
+    kc = d["key_cache"].cpu()
+    vc = d["value_cache"].cpu()
+    # decode rows: the longest, the shortest and a seeded sample
+    ctx = w.context_lens[w.decode_rows]
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[int(ctx.argmax()), int(ctx.argmin())],
+                                     rng.choice(len(w.decode_rows), 6, replace=False)]))
+    ref = oracle_decode(w, kc, vc, rows)
+    err = max_err(out[torch.from_numpy(rows).to(gpu)], ref)
+    say(f"full workload {name}: decode max abs err {err:.3e} over rows {rows.tolist()}")
+    assert err <= TOL[w.dtype]
+    assert torch.isfinite(out).all()
+    if len(w.prefill_rows):
+        refp = oracle_prefill(w, kc, vc)
+        errp = max_err(pre, refp)
+        say(f"full workload {name}: prefill max abs err {errp:.3e}")
+        assert errp <= TOL[w.dtype]
