@@ -47,7 +47,7 @@ struct RowLayout {
 
 template <typename E, int D, int GT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
-    DecodeArgs a, int32_t head_chunks, uint32_t n_logical, uint32_t per_xcd, float scale_log2) {
+    DecodeArgs a, int32_t head_chunks, uint32_t n_logical, float scale_log2) {
   using R = RowLayout<E, D>;
   constexpr int EPL = R::kEpl, LPT = R::kLpt, TPL = R::kTpl, U = R::kUnroll, TILE = R::kTile;
 
@@ -57,17 +57,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   __shared__ float s_sum[kWaves][GT];
   __shared__ float s_acc[kWaves][GT][D];
 
-  // Logical order ((seq * Hkv + kv_head) * P + part) * chunks + chunk keeps one
-  // sequence's work on one XCD (its L2), in sequence order.
-  const uint32_t logical = xcd_remap(blockIdx.x, per_xcd);
+  // Work order ((part * S + seq) * Hkv + kv_head) * chunks + chunk, dispatched
+  // round-robin over the 8 XCDs: every XCD receives an even share of every
+  // partition index and of every sequence, so ragged lengths stay balanced
+  // across XCDs (a contiguous range of whole sequences per XCD does not).
+  const uint32_t logical = blockIdx.x;
   if (logical >= n_logical) return;
   uint32_t rem = logical;
   const int chunk = rem % head_chunks;
   rem /= head_chunks;
-  const int part = rem % a.num_parts;
-  rem /= a.num_parts;
   const int kvh = rem % a.num_kv_heads;
-  const int seq = rem / a.num_kv_heads;
+  rem /= a.num_kv_heads;
+  const int seq = rem % a.num_seqs;
+  const int part = rem / a.num_seqs;
 
   const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
   const int nparts = max(1, (ctx + a.part_tokens - 1) / a.part_tokens);
@@ -279,10 +281,10 @@ hipError_t launch_partitions_gt(const DecodeArgs& a, hipStream_t stream) {
   const int chunks = (group + GT - 1) / GT;
   const uint64_t n = static_cast<uint64_t>(a.num_seqs) * a.num_kv_heads * a.num_parts * chunks;
   if (n == 0) return hipSuccess;
-  const uint32_t per = static_cast<uint32_t>((n + 7) / 8);
   const float scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((decode_partition_kernel<E, D, GT>), dim3(per * 8), dim3(kDecodeThreads), 0,
-                     stream, a, chunks, static_cast<uint32_t>(n), per, scale_log2);
+  hipLaunchKernelGGL((decode_partition_kernel<E, D, GT>), dim3(static_cast<uint32_t>(n)),
+                     dim3(kDecodeThreads), 0, stream, a, chunks, static_cast<uint32_t>(n),
+                     scale_log2);
   return hipGetLastError();
 }
 
@@ -340,11 +342,8 @@ DecodeWorkspace decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream) {
-  switch (a.dtype) {
-    case PA_DTYPE_F32: return launch_partitions_e<F32>(a, stream);
-    case PA_DTYPE_F16: return launch_partitions_e<F16>(a, stream);
-    default: return launch_partitions_e<BF16>(a, stream);
-  }
+  if (a.dtype == PA_DTYPE_F32) return launch_partitions_e<F32>(a, stream);
+  return launch_decode_rows(a, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {

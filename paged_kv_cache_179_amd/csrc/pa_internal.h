@@ -83,6 +83,8 @@ struct PrefillArgs {
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+// 16-bit caches: one-token-per-lane score layout (decode_rows.hip).
+hipError_t launch_decode_rows(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 struct PrefillWorkspace {
   size_t bytes;
