@@ -292,6 +292,14 @@ def _cpu_model():
 # ---------------------------------------------------------------------------
 # Counter-derived traffic (committed rocprofv3 summaries).
 # ---------------------------------------------------------------------------
+def partition_kernel_name(w):
+    """Symbol of the decode partition kernel that serves workload w."""
+    g = w.num_heads // w.num_kv_heads
+    if w.dtype == "fp32":
+        return f"decode_partition_kernel<F32,{w.head_dim},...>"
+    return f"decode_rows_kernel<{w.dtype.upper().replace('FP', 'F')},{w.head_dim},{g}>"
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "paged_kv_cache_179_amd", "csrc"))):
@@ -429,7 +437,7 @@ def main():
                    "num_blocks": w.num_blocks},
         "hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
         "attended_tokens_per_s": round(r["decode_attended_tokens_per_s"], 1),
-        "roofline": {"kernel": "decode_partition_kernel", "bound": "hbm",
+        "roofline": {"kernel": partition_kernel_name(w), "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "avg_launch_ms": round(part_ms, 5),
