@@ -32,6 +32,12 @@ HIPCC_FLAGS = [
     f"-I{REPO / 'include'}",
     f"-I{CSRC}",
 ]
+# Per-source extras.  The MFMA decode kernel rescales its accumulators with
+# vector ALU ops inside the loop; keeping MFMA results in ordinary VGPRs (not
+# AGPRs) avoids a copy of every accumulator in and out on each pass.
+EXTRA_FLAGS = {
+    "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:
@@ -47,7 +53,7 @@ def sources():
 
 def _compile(src: Path, verbose: bool) -> Path:
     obj = BUILD / (src.name + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", str(src), "-o", str(obj)]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src.name, []), "-c", str(src), "-o", str(obj)]
     if src.suffix == ".cpp":
         cmd.insert(1, "-x")
         cmd.insert(2, "hip")

@@ -27,7 +27,10 @@
 // them: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
 // Scores are kept in log2 units (scale * log2(e) folded in) so every
 // exponential is one v_exp_f32.
+#include <algorithm>
+
 #include "device_common.h"
+#include "decode_common.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -47,7 +50,7 @@ struct RowLayout {
 
 template <typename E, int D, int GT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
-    DecodeArgs a, int32_t head_chunks, uint32_t n_logical, float scale_log2) {
+    DecodeArgs a, int32_t head_chunks, float scale_log2) {
   using R = RowLayout<E, D>;
   constexpr int EPL = R::kEpl, LPT = R::kLpt, TPL = R::kTpl, U = R::kUnroll, TILE = R::kTile;
 
@@ -57,23 +60,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   __shared__ float s_sum[kWaves][GT];
   __shared__ float s_acc[kWaves][GT][D];
 
-  // Work order ((part * S + seq) * Hkv + kv_head) * chunks + chunk, dispatched
-  // round-robin over the 8 XCDs: every XCD receives an even share of every
-  // partition index and of every sequence, so ragged lengths stay balanced
-  // across XCDs (a contiguous range of whole sequences per XCD does not).
-  const uint32_t logical = blockIdx.x;
-  if (logical >= n_logical) return;
-  uint32_t rem = logical;
-  const int chunk = rem % head_chunks;
-  rem /= head_chunks;
-  const int kvh = rem % a.num_kv_heads;
-  rem /= a.num_kv_heads;
-  const int seq = rem % a.num_seqs;
-  const int part = rem / a.num_seqs;
-
-  const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
+  const DecodeItem item = decode_item(a, head_chunks);
+  if (!item.valid) return;
+  const int seq = item.seq, part = item.part, ctx = item.ctx, kvh = item.kvh, chunk = item.chunk;
   const int nparts = max(1, (ctx + a.part_tokens - 1) / a.part_tokens);
-  if (part >= nparts) return;
 
   const int group = a.num_heads / a.num_kv_heads;
   const int h_first = kvh * group + chunk * GT;
@@ -279,12 +269,12 @@ template <typename E, int D, int GT>
 hipError_t launch_partitions_gt(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_heads / a.num_kv_heads;
   const int chunks = (group + GT - 1) / GT;
-  const uint64_t n = static_cast<uint64_t>(a.num_seqs) * a.num_kv_heads * a.num_parts * chunks;
+  const uint64_t n = decode_grid(a, chunks);
   if (n == 0) return hipSuccess;
+  if (n > 0x7fffffffu) return hipErrorInvalidValue;
   const float scale_log2 = a.scale * kLog2e;
   hipLaunchKernelGGL((decode_partition_kernel<E, D, GT>), dim3(static_cast<uint32_t>(n)),
-                     dim3(kDecodeThreads), 0, stream, a, chunks, static_cast<uint32_t>(n),
-                     scale_log2);
+                     dim3(kDecodeThreads), 0, stream, a, chunks, scale_log2);
   return hipGetLastError();
 }
 
@@ -312,6 +302,61 @@ hipError_t launch_partitions_e(const DecodeArgs& a, hipStream_t stream) {
   }
 }
 
+// Work plan: every non-empty (sequence, partition) item, ordered longest
+// first.  The partial last partitions come after the full ones, in decreasing
+// length, so the short ones fill the tail of the partition kernel instead of
+// a long one starting last.  A counting sort over kPlanBuckets length classes
+// (descending); the order inside a class is whatever the LDS atomics give,
+// which changes only the dispatch order, never a result.  One workgroup.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 64;
+
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
+  __shared__ int hist[kPlanBuckets];
+  const int tid = threadIdx.x;
+  if (tid < kPlanBuckets) hist[tid] = 0;
+  __syncthreads();
+
+  const int P = a.part_tokens;
+  int shift = 0;
+  while (((P - 1) >> shift) >= kPlanBuckets) ++shift;
+  const int64_t n = static_cast<int64_t>(a.num_seqs) * a.num_parts;
+  // Item i is partition i / S of sequence i % S: partition-major, so that
+  // within a class, items of neighbouring sequences stay close together.
+  auto tokens = [&](int64_t i, int* seq, int* part, int* ctx) {
+    *part = static_cast<int>(i / a.num_seqs);
+    *seq = static_cast<int>(i - static_cast<int64_t>(*part) * a.num_seqs);
+    *ctx = max(0, min(a.context_lens[*seq], a.ctx_limit));
+    const int t = min(P, *ctx - *part * P);
+    // A sequence with an empty context still owns one item (partition 0):
+    // its output rows are written as zeros.
+    return (*part == 0 && *ctx == 0) ? 1 : t;
+  };
+  for (int64_t i = tid; i < n; i += kPlanThreads) {
+    int seq, part, ctx;
+    const int t = tokens(i, &seq, &part, &ctx);
+    if (t > 0) atomicAdd(&hist[kPlanBuckets - 1 - ((t - 1) >> shift)], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int b = 0; b < kPlanBuckets; ++b) {
+      const int c = hist[b];
+      hist[b] = run;
+      run += c;
+    }
+    *a.plan_count = run;
+  }
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += kPlanThreads) {
+    int seq, part, ctx;
+    const int t = tokens(i, &seq, &part, &ctx);
+    if (t <= 0) continue;
+    const int pos = atomicAdd(&hist[kPlanBuckets - 1 - ((t - 1) >> shift)], 1);
+    a.plan[pos] = make_int4(seq, part, 1, ctx);
+  }
+}
+
 template <typename E>
 hipError_t launch_reduce_e(const DecodeArgs& a, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_heads;
@@ -332,17 +377,28 @@ static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 DecodeWorkspace decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                         int32_t num_parts) {
   DecodeWorkspace w{};
-  if (num_parts <= 1 || num_seqs <= 0) return w;
-  const size_t n = static_cast<size_t>(num_seqs) * num_heads * num_parts;
-  w.off_max = 0;
-  w.off_sum = align256(n * sizeof(float));
-  w.off_acc = w.off_sum + align256(n * sizeof(float));
-  w.bytes = w.off_acc + align256(n * head_dim * sizeof(float));
+  if (num_seqs <= 0) return w;
+  size_t off = 0;
+  if (num_parts > 1) {
+    const size_t n = static_cast<size_t>(num_seqs) * num_heads * num_parts;
+    w.off_max = 0;
+    w.off_sum = align256(n * sizeof(float));
+    w.off_acc = w.off_sum + align256(n * sizeof(float));
+    off = w.off_acc + align256(n * head_dim * sizeof(float));
+  }
+  w.off_count = off;
+  w.off_plan = off + 256;
+  w.bytes = w.off_plan + align256(static_cast<size_t>(num_seqs) * std::max(num_parts, 1) * sizeof(int4));
   return w;
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_seqs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (a.dtype == PA_DTYPE_F32) return launch_partitions_e<F32>(a, stream);
+  if (a.num_heads / a.num_kv_heads >= kMfmaMinGroup) return launch_decode_mfma(a, stream);
   return launch_decode_rows(a, stream);
 }
 

@@ -1,0 +1,41 @@
+// Work items of the decode partition kernels.
+//
+// A planning kernel lists every non-empty (sequence, partition) pair, longest
+// first, before the partition kernel runs.  Workgroup b of the partition
+// kernel then takes item b / (Hkv * head_chunks) of that list, for KV head and
+// head chunk b % (Hkv * head_chunks).  The grid is sized for the worst case
+// (every sequence at the full context), so the workgroups past the end of the
+// list, all at the end of the grid, exit at once.
+#pragma once
+
+#include "pa_internal.h"
+
+namespace pa {
+
+struct DecodeItem {
+  int seq, part, ctx, kvh, chunk;
+  bool valid;
+};
+
+__device__ inline DecodeItem decode_item(const DecodeArgs& a, int head_chunks) {
+  const uint32_t per = static_cast<uint32_t>(a.num_kv_heads * head_chunks);
+  const uint32_t j = blockIdx.x / per;
+  const uint32_t r = blockIdx.x - j * per;
+  const int count = *a.plan_count;
+  const int4 it = a.plan[j];  // in bounds: the grid has S * P * per workgroups
+  DecodeItem d;
+  d.valid = static_cast<int>(j) < count;
+  d.seq = it.x;
+  d.part = it.y;
+  d.ctx = it.w;
+  d.kvh = static_cast<int>(r) / head_chunks;
+  d.chunk = static_cast<int>(r) - d.kvh * head_chunks;
+  return d;
+}
+
+// Grid of a partition kernel: one workgroup per possible item and KV head chunk.
+inline uint64_t decode_grid(const DecodeArgs& a, int head_chunks) {
+  return static_cast<uint64_t>(a.num_seqs) * a.num_parts * a.num_kv_heads * head_chunks;
+}
+
+}  // namespace pa

@@ -1,0 +1,482 @@
+// Paged-attention decode for grouped-query heads on the matrix cores.
+//
+// Same operation, work split, partition states and reduce as the other decode
+// kernels: the PagedAttention decode of the wLLM PyPI page ("Features -- Core
+// engine"), with the grouped-query mapping of the mini-vLLM README ("End-to-end
+// throughput vs baselines": each query head reads its KV head).  When G query
+// heads share a KV head, every cached element feeds 2G flops.  q.k and p.V
+// are then a real [G x D] x [D x T] contraction, so both run on MFMA:
+//
+// * A pass is one 16-token tile.  Its K and V rows are copied HBM -> LDS by the
+//   gfx950 global-to-LDS DMA, as in the vector kernel: two slots per wave,
+//   with the next pass in flight while this one is computed.  The block id of
+//   a pass comes through a scalar load, so the only vector-memory operations
+//   in flight are the DMAs that the explicit waits count.
+// * Scores: S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}.  The A operand is
+//   the tile's key rows, one 16-byte LDS read per lane per 32 dims.  The B
+//   operand is the group's query rows, loaded once into registers; up to 16
+//   heads, unused heads are zero.  Lane l ends up with the scores of head
+//   l % 16 for tokens 4 * (l / 16) + 0..3.
+// * Probabilities, rounded to the cache type, are then already laid out as
+//   the B operand of O^T += V^T P^T with v_mfma_f32_16x16x16: no exchange
+//   between lanes.  The A operand V^T comes from LDS through the gfx950
+//   transposing read (ds_read_b64_tr_b16): four tokens of one value column
+//   per lane.  One more MFMA against a ones operand sums the same rounded
+//   probabilities for the denominator.
+// * Online softmax in base 2 with lazy rescaling.  The running max of a head
+//   only moves when a score passes it by more than 2^8, so probabilities stay
+//   <= 256.
+// * Key and value rows are stored in LDS with their 16-byte chunks rotated
+//   per row.  Keys: chunk c of row t at (c - t) mod NC.  Values: at
+//   (c - 2t) mod NC, or (c - (t & ~1)) mod 8 at head_dim 64.  With these, the
+//   16 lanes of a key read, and the 32 lanes of a transposing value read, hit
+//   distinct banks.
+//
+// The kernel is persistent: as many workgroups as fit on the device, each
+// looping over work units (one (sequence, partition) item of the plan, one KV
+// head, up to 16 of its query heads), statically: units b, b + grid, ...
+// Four waves take the unit's 16-token passes in turn and merge through LDS at
+// the end of the unit; the first pass of the next unit is already in flight
+// by then.
+#include <algorithm>
+#include <atomic>
+
+#include "device_common.h"
+#include "lds_dma.h"
+#include "decode_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = kDecodeThreads / kWave;
+constexpr int kTile = 16;       // tokens per pass
+constexpr int kHeadTile = 16;   // query heads per workgroup (MFMA N)
+constexpr float kLazyMax = 8.f; // log2 of the largest unnormalised probability
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+template <typename E>
+struct Mma;
+template <>
+struct Mma<BF16> {
+  static constexpr unsigned kOnePair = 0x3F803F80u;
+  __device__ static inline f32x4 qk(const u32x4& k, const u32x4& q, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                   __builtin_bit_cast(bf16x8, q), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 pv(const u32x2& v, const u32x2& p, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v),
+                                                     __builtin_bit_cast(s16x4, p), c, 0, 0, 0);
+  }
+  __device__ static inline unsigned pack(float lo, float hi) {
+    const bf16x2 r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(unsigned, r);
+  }
+};
+template <>
+struct Mma<F16> {
+  static constexpr unsigned kOnePair = 0x3C003C00u;
+  __device__ static inline f32x4 qk(const u32x4& k, const u32x4& q, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                  __builtin_bit_cast(f16x8, q), c, 0, 0, 0);
+  }
+  __device__ static inline f32x4 pv(const u32x2& v, const u32x2& p, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v),
+                                                 __builtin_bit_cast(f16x4, p), c, 0, 0, 0);
+  }
+  __device__ static inline unsigned pack(float lo, float hi) {
+    const f16x2 r = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+    return __builtin_bit_cast(unsigned, r);
+  }
+};
+
+template <int D>
+struct TileGeo {
+  static constexpr int NC = D / 8;           // 16-byte chunks per row
+  static constexpr int RB = 2 * D;           // row bytes
+  static constexpr int RPI = 1024 / RB;      // rows per DMA instruction
+  static constexpr int NDMA = kTile / RPI;   // DMA instructions per pass, K or V
+  static constexpr int KB = D / 32;          // q.k MFMAs per pass
+  static constexpr int MT = D / 16;          // p.V MFMAs per pass
+  __device__ static inline int rot_k(int t) { return t % NC; }
+  __device__ static inline int rot_v(int t) { return D == 64 ? (t & ~1) % NC : (2 * t) % NC; }
+};
+
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48.  Each swap hands a lane its own
+// value and its partner's (in some order), so the max of the two is the pair max.
+__device__ inline float max_across_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Read-only data loaded through the scalar unit: the work plan, its length and
+// the block tables.  Scalar loads are counted by lgkmcnt, apart from the
+// vector-memory counter that orders the DMA pipeline.
+typedef __attribute__((address_space(4))) const int32_t cint;
+
+template <typename T>
+__device__ inline T scalar_ptr(const void* p) {
+  return reinterpret_cast<T>(reinterpret_cast<uintptr_t>(p));
+}
+
+// One work unit: one (sequence, partition) item of the plan, for one KV head
+// and one chunk of up to 16 of its query heads.  All fields are wave-uniform.
+struct Unit {
+  bool valid;
+  int seq, kvh, h_first, nh;
+  int tb, te, ctx;  // token range [tb, te) of the partition; context length
+  int mine;         // passes of this wave (passes w, w + 4, ... of the unit)
+};
+
+template <typename E, int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs a, int32_t head_chunks,
+                                                                     float scale_log2) {
+  using M = Mma<E>;
+  using G = TileGeo<D>;
+  constexpr int NC = G::NC, RB = G::RB, RPI = G::RPI, NDMA = G::NDMA, KB = G::KB, MT = G::MT;
+  constexpr int NQ = kHeadTile * RB / 1024;  // DMA instructions per query tile
+  
+  // Per wave, two pipeline slots, each a key tile and a value tile of
+  // [kTile rows][NC chunks].  A slot is exactly one wave's partial output
+  // [16 heads][D] in fp32, which is where that goes at the end of a unit.
+  __shared__ u32x4 s_kv[kWaves][2][2][kTile][NC];
+  // Query tile of the current unit and of the next one.
+  __shared__ u32x4 s_q[2][kHeadTile][NC];
+  __shared__ float s_max[kWaves][kHeadTile];
+  __shared__ float s_sum[kWaves][kHeadTile];
+  __shared__ int s_part[kWaves];
+  static_assert(sizeof(s_kv[0][0]) == kHeadTile * D * sizeof(float), "partial output fills a slot");
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hl = lane & 15;  // head (scores, outputs); key row (score A operand)
+  const int g4 = lane >> 4;  // 16-lane row of the wave
+
+  const int per = a.num_kv_heads * head_chunks;
+  const int n_units = *scalar_ptr<cint*>(a.plan_count) * per;
+  int u = blockIdx.x;
+  if (u >= n_units) return;
+  const int stride = gridDim.x;
+
+  const int group = a.num_heads / a.num_kv_heads;
+  const int P = a.part_tokens;
+  const int lbs = a.log2_block_size;
+  const int off_mask = (1 << lbs) - 1;
+  const char* kbase = static_cast<const char*>(a.key_cache);
+  const char* vbase = static_cast<const char*>(a.value_cache);
+  const char* qbase = static_cast<const char*>(a.query);
+  cint* plan = scalar_ptr<cint*>(a.plan);  // [item][seq, part, run, ctx]
+  cint* tables = scalar_ptr<cint*>(a.block_tables);
+
+  auto info = [&](int uu) {
+    Unit x;
+    x.valid = uu < n_units;
+    const int j = x.valid ? uu / per : 0;
+    const int r = x.valid ? uu - j * per : 0;
+    x.seq = plan[4 * static_cast<int64_t>(j)];
+    x.ctx = plan[4 * static_cast<int64_t>(j) + 3];
+    x.kvh = r / head_chunks;
+    const int chunk = r - x.kvh * head_chunks;
+    x.h_first = x.kvh * group + chunk * kHeadTile;
+    x.nh = min(kHeadTile, group - chunk * kHeadTile);
+    x.tb = plan[4 * static_cast<int64_t>(j) + 1] * P;
+    x.te = min(x.tb + P, x.ctx);
+    const int npass = (x.valid && x.te > x.tb) ? (x.te - x.tb + kTile - 1) / kTile : 0;
+    x.mine = npass > wave ? (npass - wave + kWaves - 1) / kWaves : 0;
+    return x;
+  };
+
+  // Per-lane LDS offsets of the compute reads (bytes within one tile).  Key
+  // and query rows share the rotation (chunk c of row t at (c - t) mod NC).
+  int koff[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) koff[kb] = hl * RB + ((4 * kb + g4 - G::rot_k(hl) + NC) % NC) * 16;
+  int voff[MT];
+  {
+    const int vrow = 4 * g4 + (hl >> 2);
+    const int q4 = hl & 3;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      voff[mt] = vrow * RB + ((2 * mt + (q4 >> 1) - G::rot_v(vrow) + NC) % NC) * 16 + (q4 & 1) * 8;
+  }
+
+  // DMA of pass k of unit x (tokens x.tb + (4 k + wave) * 16 ...) into slot
+  // `sl`.  Rows past the partition are clamped to its last token (read, then
+  // given probability 0).
+  auto issue = [&](const Unit& x, int k, int sl) {
+    const int t0 = x.tb + (k * kWaves + wave) * kTile;
+    const char* kd = reinterpret_cast<const char*>(&s_kv[wave][sl][0][0][0]);
+    const char* vd = reinterpret_cast<const char*>(&s_kv[wave][sl][1][0][0]);
+    const int64_t trow = static_cast<int64_t>(x.seq) * a.max_blocks_per_seq;
+    if (lbs >= 4) {
+      // The 16 tokens lie in one block: one scalar table read per pass.
+      int b = tables[trow + (t0 >> lbs)];
+      b = (b < 0 || b >= a.num_blocks) ? 0 : b;
+      const int64_t head_off = ((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) * RB;
+#pragma unroll
+      for (int r = 0; r < NDMA; ++r) {
+        const int row = r * RPI + lane / NC;
+        const int pos = lane % NC;
+        const int t = min(t0 + row, x.te - 1);
+        const int64_t roff = head_off + static_cast<int64_t>(t & off_mask) * RB;
+        dma16(kbase + roff + ((pos + G::rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+        dma16(vbase + roff + ((pos + G::rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+      }
+    } else {
+      // Small blocks: each row reads its own table entry (vector loads; the
+      // compiler then waits for them before the DMA, which is correct but
+      // drains the pipeline -- a layout kept for completeness, not speed).
+#pragma unroll
+      for (int r = 0; r < NDMA; ++r) {
+        const int row = r * RPI + lane / NC;
+        const int pos = lane % NC;
+        const int t = min(t0 + row, x.te - 1);
+        int b = a.block_tables[trow + (t >> lbs)];
+        b = (b < 0 || b >= a.num_blocks) ? 0 : b;
+        const int64_t roff =
+            (((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) | (t & off_mask)) * RB;
+        dma16(kbase + roff + ((pos + G::rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+        dma16(vbase + roff + ((pos + G::rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+      }
+    }
+  };
+
+  // DMA of unit x's query rows into query buffer `qb` (wave 0 only).  Rows
+  // past the head chunk repeat its last row; their outputs are never written.
+  auto issue_q = [&](const Unit& x, int qb) {
+    const char* qd = reinterpret_cast<const char*>(&s_q[qb][0][0]);
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+      const int row = r * RPI + lane / NC;
+      const int pos = lane % NC;
+      const int h = min(row, x.nh - 1);
+      const char* src = qbase + (static_cast<int64_t>(x.seq) * a.num_heads + x.h_first + h) * RB;
+      dma16(src + ((pos + G::rot_k(row)) % NC) * 16, qd + r * RPI * RB);
+    }
+  };
+
+  const u32x2 ones = {M::kOnePair, M::kOnePair};
+  f32x4 acc[MT];
+  f32x4 lacc;
+  float m;
+
+  auto compute = [&](const Unit& x, int k, int sl, int qb) {
+    const int t0 = x.tb + (k * kWaves + wave) * kTile;
+    const char* kt = reinterpret_cast<const char*>(&s_kv[wave][sl][0][0][0]);
+    const char* vt = reinterpret_cast<const char*>(&s_kv[wave][sl][1][0][0]);
+    const char* qt = reinterpret_cast<const char*>(&s_q[qb][0][0]);
+
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      s = M::qk(*reinterpret_cast<const u32x4*>(kt + koff[kb]),
+                *reinterpret_cast<const u32x4*>(qt + koff[kb]), s);
+
+    // Lane (hl, g4) holds head hl's scores of tokens t0 + 4 g4 + i.
+    float sc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[i] = t0 + 4 * g4 + i < x.te ? s[i] * scale_log2 : -__builtin_inff();
+    const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazyMax) != 0) {  // wave-uniform
+      const float m_new = fmaxf(m, mx);
+      const float alpha = exp2_fast(m - m_new);  // 0 on the first update
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+      lacc *= alpha;
+      m = m_new;
+    }
+    const u32x2 pb = {M::pack(exp2_fast(sc[0] - m), exp2_fast(sc[1] - m)),
+                      M::pack(exp2_fast(sc[2] - m), exp2_fast(sc[3] - m))};
+    lacc = M::pv(ones, pb, lacc);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff[mt]));
+      acc[mt] = M::pv(__builtin_bit_cast(u32x2, v), pb, acc[mt]);
+    }
+    wave_lds_sync();
+  };
+
+  // Merge of the four waves' partial states of unit x (slot `pr` of each
+  // wave holds its partial output) and the output or workspace writes.
+  auto finish = [&](const Unit& x, int pr) {
+    float* part_out = reinterpret_cast<float*>(&s_kv[wave][pr][0][0][0]);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<f32x4*>(part_out + hl * D + 16 * mt + 4 * g4) = acc[mt];
+    if (lane < kHeadTile) {
+      s_max[wave][hl] = m;
+      s_sum[wave][hl] = lacc[0];
+    }
+    if (lane == 0) s_part[wave] = pr;
+    __syncthreads();
+    const int nparts = max(1, (x.ctx + P - 1) / P);
+    const int part = x.tb / P;
+    // Four consecutive dims of one head per thread and step.
+    constexpr int D4 = D / 4;
+    for (int idx = tid; idx < x.nh * D4; idx += kDecodeThreads) {
+      const int h = idx / D4;
+      const int d = (idx - h * D4) * 4;
+      float mw[kWaves];
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        mw[w] = s_max[w][h];
+        mx = fmaxf(mx, mw[w]);
+      }
+      const float mu = safe_max(mx);
+      float den = 0.f;
+      f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = exp2_fast(mw[w] - mu);
+        den = __builtin_fmaf(f, s_sum[w][h], den);
+        num += f * *reinterpret_cast<const f32x4*>(
+                       reinterpret_cast<const float*>(&s_kv[w][s_part[w]][0][0][0]) + h * D + d);
+      }
+      const int64_t row = static_cast<int64_t>(x.seq) * a.num_heads + x.h_first + h;
+      if (nparts == 1) {
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+        if (den != 0.f) o = num / den;
+        const u32x2 packed = {M::pack(o[0], o[1]), M::pack(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(static_cast<char*>(a.out) + (row * D + d) * 2) = packed;
+      } else {
+        const int64_t ws = row * a.num_parts + part;
+        *reinterpret_cast<f32x4*>(a.ws_acc + ws * D + d) = num;
+        if (d == 0) {
+          a.ws_max[ws] = mx;
+          a.ws_sum[ws] = den;
+        }
+      }
+    }
+    __syncthreads();
+  };
+
+  // Persistent loop over units u, u + grid, u + 2 grid, ... (the plan is
+  // ordered longest first, so every round of the grid takes units of similar
+  // length).  Each wave keeps one DMA in flight ahead of the pass it
+  // computes, and the first pass of the next unit is issued before the
+  // current unit's merge, so its latency overlaps the merge.  Wave 0 also
+  // stages the next unit's query rows; those NQ DMAs are ordered before a
+  // pass's and waited with it.
+  Unit cur = info(u);
+  Unit nxt = info(u + stride);
+  int qb = 0;
+  if (wave == 0) {
+    issue_q(cur, 0);
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  int slot = 0;
+  if (cur.mine > 0) issue(cur, 0, slot);
+  while (true) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+    m = -__builtin_inff();
+    bool q_todo = wave == 0 && nxt.valid;
+    const bool next_first = nxt.valid && nxt.mine > 0;
+    for (int k = 0; k < cur.mine; ++k) {
+      if (k + 1 < cur.mine) {
+        issue(cur, k + 1, slot ^ 1);
+        if (q_todo) {
+          issue_q(nxt, qb ^ 1);  // waited by the next iteration's wait
+          q_todo = false;
+          wait_vmcnt<2 * NDMA + NQ>();
+        } else {
+          wait_vmcnt<2 * NDMA>();
+        }
+      } else {
+        if (q_todo) {
+          issue_q(nxt, qb ^ 1);  // older than the pass below: waited with it
+          q_todo = false;
+        }
+        if (next_first) {
+          issue(nxt, 0, slot ^ 1);
+          wait_vmcnt<2 * NDMA>();
+        } else {
+          wait_vmcnt<0>();
+        }
+      }
+      wave_lds_sync();
+      compute(cur, k, slot, qb);
+      slot ^= 1;
+    }
+    if (cur.mine == 0) {
+      if (q_todo) issue_q(nxt, qb ^ 1);
+      if (next_first) {
+        issue(nxt, 0, slot);
+        wait_vmcnt<2 * NDMA>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    // Now only the next unit's first pass (if any) is in flight, in `slot`;
+    // the next query tile has landed.
+    finish(cur, slot ^ 1);
+    if (!nxt.valid) break;
+    u += stride;
+    cur = nxt;
+    nxt = info(u + stride);
+    qb ^= 1;
+  }
+}
+
+// Workgroups of one persistent launch: as many as fit on the device at once.
+template <typename E, int D>
+int persistent_grid() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int g = cache[dev].load(std::memory_order_relaxed);
+  if (g > 0) return g;
+  int ncu = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 1;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D>, kDecodeThreads, 0) !=
+      hipSuccess)
+    per_cu = 1;
+  g = std::max(1, ncu) * std::max(1, per_cu);
+  cache[dev].store(g, std::memory_order_relaxed);
+  return g;
+}
+
+template <typename E, int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  const int group = a.num_heads / a.num_kv_heads;
+  const int chunks = (group + kHeadTile - 1) / kHeadTile;
+  const uint64_t n = decode_grid(a, chunks);
+  if (n == 0) return hipSuccess;
+  const uint64_t grid = std::min<uint64_t>(n, static_cast<uint64_t>(persistent_grid<E, D>()));
+  hipLaunchKernelGGL((decode_mfma_kernel<E, D>), dim3(static_cast<uint32_t>(grid)), dim3(kDecodeThreads),
+                     0, stream, a, chunks, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_e(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 64: return launch_d<E, 64>(a, stream);
+    case 128: return launch_d<E, 128>(a, stream);
+    case 256: return launch_d<E, 256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+  if (a.dtype == PA_DTYPE_BF16) return launch_e<BF16>(a, stream);
+  if (a.dtype == PA_DTYPE_F16) return launch_e<F16>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -31,6 +31,8 @@
 // chunk); the waves take the passes of each 512-token segment in turn and are
 // merged through LDS at the end.
 #include "device_common.h"
+#include "lds_dma.h"
+#include "decode_common.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -100,41 +102,8 @@ struct Geo {
   __device__ static inline int rot(int t) { return D == 64 ? (LQ * (t >> 1)) % NC : (LQ * t) % NC; }
 };
 
-// s_waitcnt immediate with vmcnt = N (N < 16), expcnt and lgkmcnt not waited.
-template <int N>
-__device__ inline void wait_vmcnt() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
-// 16-byte global-to-LDS DMA (non-temporal).  `lds` is the wave-uniform LDS
-// destination of lane 0; lane i's 16 bytes land at lds + 16 * i.  Written as
-// inline assembly so that the compiler does not treat every later LDS read as
-// dependent on every outstanding DMA (it cannot tell the pipeline slots apart
-// and would wait for all of them); the kernel orders each slot with explicit
-// vmcnt waits.  M0 carries the LDS address; nothing else in these kernels
-// keeps a value in M0.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void dma16(const void* global, const void* lds) {
-  const uint32_t off = static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(global)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <typename E, int D, int GT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(DecodeArgs a, int32_t head_chunks,
-                                                                     uint32_t n_logical,
                                                                      float scale_log2) {
   using P = Pack16<E>;
   using G = Geo<D>;
@@ -162,19 +131,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(DecodeArgs 
     return base[h * D + d];
   };
 
-  const uint32_t logical = blockIdx.x;
-  if (logical >= n_logical) return;
-  uint32_t rem = logical;
-  const int chunk = rem % head_chunks;
-  rem /= head_chunks;
-  const int kvh = rem % a.num_kv_heads;
-  rem /= a.num_kv_heads;
-  const int seq = rem % a.num_seqs;
-  const int part = rem / a.num_seqs;
-
-  const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
+  const DecodeItem item = decode_item(a, head_chunks);
+  if (!item.valid) return;
+  const int seq = item.seq, part = item.part, ctx = item.ctx, kvh = item.kvh, chunk = item.chunk;
   const int nparts = max(1, (ctx + a.part_tokens - 1) / a.part_tokens);
-  if (part >= nparts) return;
 
   const int group = a.num_heads / a.num_kv_heads;
   const int h_first = kvh * group + chunk * GT;
@@ -390,11 +350,11 @@ template <typename E, int D, int GT>
 hipError_t launch_gt(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_heads / a.num_kv_heads;
   const int chunks = (group + GT - 1) / GT;
-  const uint64_t n = static_cast<uint64_t>(a.num_seqs) * a.num_kv_heads * a.num_parts * chunks;
+  const uint64_t n = decode_grid(a, chunks);
   if (n == 0) return hipSuccess;
+  if (n > 0x7fffffffu) return hipErrorInvalidValue;
   hipLaunchKernelGGL((decode_rows_kernel<E, D, GT>), dim3(static_cast<uint32_t>(n)),
-                     dim3(kDecodeThreads), 0, stream, a, chunks, static_cast<uint32_t>(n),
-                     a.scale * kLog2e);
+                     dim3(kDecodeThreads), 0, stream, a, chunks, a.scale * kLog2e);
   return hipGetLastError();
 }
 

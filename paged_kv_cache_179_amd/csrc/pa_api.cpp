@@ -100,9 +100,11 @@ pa_status decode_args(void* out, const void* query, const void* key_cache, const
   a->value_cache = value_cache;
   a->block_tables = block_tables;
   a->context_lens = context_lens;
-  a->ws_max = w.bytes ? reinterpret_cast<float*>(ws + w.off_max) : nullptr;
-  a->ws_sum = w.bytes ? reinterpret_cast<float*>(ws + w.off_sum) : nullptr;
-  a->ws_acc = w.bytes ? reinterpret_cast<float*>(ws + w.off_acc) : nullptr;
+  a->ws_max = g.num_parts > 1 ? reinterpret_cast<float*>(ws + w.off_max) : nullptr;
+  a->ws_sum = g.num_parts > 1 ? reinterpret_cast<float*>(ws + w.off_sum) : nullptr;
+  a->ws_acc = g.num_parts > 1 ? reinterpret_cast<float*>(ws + w.off_acc) : nullptr;
+  a->plan = reinterpret_cast<int4*>(ws + w.off_plan);
+  a->plan_count = reinterpret_cast<int32_t*>(ws + w.off_count);
   a->num_seqs = num_seqs;
   a->num_heads = num_heads;
   a->num_kv_heads = num_kv_heads;
@@ -198,9 +200,10 @@ pa_status pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_s
   const DecodeGeom g = decode_geom(
       std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size),
       partition_size);
+  if (g.num_parts <= 1) return PA_OK;  // the partition kernel wrote the output
   const pa::DecodeWorkspace w = pa::decode_workspace_layout(num_seqs, num_heads, head_dim, g.num_parts);
   pa_status st = check_workspace(w.bytes, workspace, workspace_bytes);
-  if (st != PA_OK || w.bytes == 0) return st;
+  if (st != PA_OK) return st;
   pa::DecodeArgs a{};
   const char* ws = static_cast<const char*>(workspace);
   a.out = out;

@@ -38,6 +38,8 @@ struct DecodeArgs {
   float* ws_max;   // [S][Hq][P] running max (log2 units)
   float* ws_sum;   // [S][Hq][P] softmax denominators
   float* ws_acc;   // [S][Hq][P][D] un-normalised partial outputs
+  int4* plan;      // [S * P] work items (seq, partition, 1, context length), longest first
+  int32_t* plan_count;  // number of valid items in `plan`
   int32_t num_seqs;
   int32_t num_heads;
   int32_t num_kv_heads;
@@ -54,7 +56,8 @@ struct DecodeArgs {
 
 struct DecodeWorkspace {
   size_t bytes;
-  size_t off_max, off_sum, off_acc;
+  size_t off_max, off_sum, off_acc;  // partition states (only when P > 1)
+  size_t off_count, off_plan;        // work plan (always)
 };
 DecodeWorkspace decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                         int32_t num_parts);
@@ -83,8 +86,12 @@ struct PrefillArgs {
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
-// 16-bit caches: one-token-per-lane score layout (decode_rows.hip).
+// 16-bit caches, vector kernel (decode_rows.hip): used below kMfmaMinGroup
+// query heads per KV head.
 hipError_t launch_decode_rows(const DecodeArgs& a, hipStream_t stream);
+// 16-bit caches, grouped-query heads on MFMA (decode_mfma.hip).
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+constexpr int kMfmaMinGroup = 2;
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 struct PrefillWorkspace {
   size_t bytes;

@@ -117,10 +117,14 @@ def test_reduce_validation(lib):
 
 def test_workspace_sizes(lib):
     f = lib.pa_decode_workspace_bytes
-    assert f(128, 32, 128, 4096, 0) == 0        # never split
-    assert f(128, 32, 128, 512, 512) == 0       # always one partition
+    a256 = lambda x: (x + 255) // 256 * 256
+    # One partition: only the work plan (a 256-byte header, then 16 bytes per item).
+    assert f(128, 32, 128, 4096, 0) == 256 + a256(128 * 16)       # never split
+    assert f(128, 32, 128, 512, 512) == 256 + a256(128 * 16)      # always one partition
+    # Eight partitions: max and sum per (seq, head, partition), D floats of
+    # partial output, then the plan with one item per (seq, partition).
     n = 128 * 32 * 8
-    expect = 2 * ((n * 4 + 255) // 256 * 256) + (n * 128 * 4 + 255) // 256 * 256
+    expect = 2 * a256(n * 4) + a256(n * 128 * 4) + 256 + a256(128 * 8 * 16)
     assert f(128, 32, 128, 4096, 512) == expect
     assert f(0, 32, 128, 4096, 512) == 0
     g = lib.pa_prefill_workspace_bytes
