@@ -1,28 +1,27 @@
 // Paged-attention decode for gfx950: one query token per sequence attends its
 // whole context, read block by block through the sequence's block table.
+// This file holds the parts shared by both element widths -- the work plan,
+// the merge of partition states (decode_reduce) -- and the fp32 partition
+// kernel; 16-bit caches use the MFMA kernel of decode_mfma.hip.
 //
 // The operation is the PagedAttention decode the wLLM PyPI page lists under
 // "Features -- Core engine" (a block-based KV cache read by a custom kernel),
 // with the grouped-query head mapping of the mini-vLLM README ("End-to-end
 // throughput vs baselines": each query head reads its KV head directly).
 //
-// Work decomposition.  One workgroup (4 waves) handles one
+// fp32 partition kernel.  One workgroup (4 waves) handles one
 // (sequence, KV head, context partition) and all query heads of that KV head
-// (up to 8; larger groups are split over several workgroups).  Its K/V bytes
-// are read exactly once per workgroup, whatever the group size.
+// (up to 8; larger groups are split over several workgroups).  Inside a
+// wave, a token's head_dim row is spread over LPT lanes that each load 16
+// contiguous bytes, so one wave-wide load covers TPL = 64 / LPT whole rows
+// and every (block, head) run of the [block][head][offset][dim] pool is read
+// with fully coalesced 16-byte loads.  q.k is a per-lane dot product followed
+// by a DPP butterfly over the LPT lanes of the row.  Each lane keeps an
+// online-softmax state (running max m, denominator l, un-normalised
+// accumulator) for its own token stream; the states are merged across the
+// wave, then across the 4 waves through LDS, at the end of the partition.
 //
-// Inside a wave, a token's head_dim row is spread over LPT lanes that each
-// load 16 contiguous bytes, so one wave-wide load covers TPL = 64 / LPT whole
-// rows and every (block, head) run of the [block][head][offset][dim] pool is
-// read with fully coalesced 16-byte loads.  q.k is a per-lane packed dot
-// product (v_dot2 for 16-bit types) followed by a DPP butterfly over the LPT
-// lanes of the row.  Each lane keeps an online-softmax state (running max m,
-// denominator l, un-normalised accumulator) for its own token stream; the
-// states are merged across the wave, then across the 4 waves through LDS, at
-// the end of the partition.  The block ids of the partition are staged in LDS
-// (512 tokens' worth at a time), and so are the group's query rows.
-//
-// A sequence that fits one partition writes its output directly; longer ones
+// A sequence that fits one partition gets its output directly; longer ones
 // write (m, l, acc) per partition to the workspace and decode_reduce merges
 // them: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.
 // Scores are kept in log2 units (scale * log2(e) folded in) so every
@@ -255,7 +254,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reduce_kernel(DecodeArg
 #pragma unroll
   for (int j = 0; j < PER; ++j) num[j] = 0.f;
   for (int p = 0; p < nparts; ++p) {
-    const float f = exp2_fast(a.ws_max[base + p] - mu);
+    const float m = a.ws_max[base + p];
+    // A partition joined to an earlier one's work item holds no state: its
+    // max is -inf, its sum 0, and its partial output was never written.
+    if (m == -__builtin_inff()) continue;
+    const float f = exp2_fast(m - mu);
     const float* src = a.ws_acc + (base + p) * D + lane * PER;
 #pragma unroll
     for (int j = 0; j < PER; ++j) num[j] = __builtin_fmaf(f, src[j], num[j]);
@@ -302,58 +305,95 @@ hipError_t launch_partitions_e(const DecodeArgs& a, hipStream_t stream) {
   }
 }
 
-// Work plan: every non-empty (sequence, partition) item, ordered longest
-// first.  The partial last partitions come after the full ones, in decreasing
-// length, so the short ones fill the tail of the partition kernel instead of
-// a long one starting last.  A counting sort over kPlanBuckets length classes
-// (descending); the order inside a class is whatever the LDS atomics give,
-// which changes only the dispatch order, never a result.  One workgroup.
+// Work plan: every non-empty work item, ordered longest first.  An item is a
+// span of 1, 2 or 4 consecutive partitions of one sequence: always 1 unless
+// a.plan_min_items > 0, and then the widest span of at most kSpanTokens
+// tokens that still leaves a.plan_min_items items (each item costs the
+// partition kernel a merge and a refill of its DMA pipeline).  The partial
+// last items come after the full ones, in decreasing length, so the short
+// ones fill the tail of the partition kernel instead of a long one starting
+// last.  A counting sort over kPlanBuckets length classes (descending); the
+// order inside a class is whatever the LDS atomics give, which changes only
+// the dispatch order, never a result.  One workgroup; it sits on the critical
+// path of every decode call, so it reads each context length once.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = 64;
+constexpr int kSpanTokens = 2048;
+constexpr int kPlanCtxCache = 8192;  // context lengths kept in LDS
 
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
-  __shared__ int hist[kPlanBuckets];
+  __shared__ int hist[3][kPlanBuckets];  // per span choice 1, 2, 4
+  __shared__ int s_ctx[kPlanCtxCache];
+  __shared__ int s_span;
   const int tid = threadIdx.x;
-  if (tid < kPlanBuckets) hist[tid] = 0;
+  if (tid < 3 * kPlanBuckets) hist[tid / kPlanBuckets][tid % kPlanBuckets] = 0;
   __syncthreads();
 
   const int P = a.part_tokens;
-  int shift = 0;
-  while (((P - 1) >> shift) >= kPlanBuckets) ++shift;
-  const int64_t n = static_cast<int64_t>(a.num_seqs) * a.num_parts;
-  // Item i is partition i / S of sequence i % S: partition-major, so that
-  // within a class, items of neighbouring sequences stay close together.
-  auto tokens = [&](int64_t i, int* seq, int* part, int* ctx) {
-    *part = static_cast<int>(i / a.num_seqs);
-    *seq = static_cast<int>(i - static_cast<int64_t>(*part) * a.num_seqs);
-    *ctx = max(0, min(a.context_lens[*seq], a.ctx_limit));
-    const int t = min(P, *ctx - *part * P);
-    // A sequence with an empty context still owns one item (partition 0):
-    // its output rows are written as zeros.
-    return (*part == 0 && *ctx == 0) ? 1 : t;
+  // log2 of the widest span considered: at most 4 partitions, kSpanTokens
+  // tokens and the partitions there are.
+  int max_k = 0;
+  if (a.plan_min_items > 0)
+    while (max_k < 2 && (P << (max_k + 1)) <= kSpanTokens && (2 << max_k) <= a.num_parts) ++max_k;
+  int shift[3] = {0, 0, 0};
+  for (int k = 0; k <= max_k; ++k)
+    while ((((P << k) - 1) >> shift[k]) >= kPlanBuckets) ++shift[k];
+  auto ctx_of = [&](int s) {
+    return s < kPlanCtxCache ? s_ctx[s] : max(0, min(a.context_lens[s], a.ctx_limit));
   };
-  for (int64_t i = tid; i < n; i += kPlanThreads) {
-    int seq, part, ctx;
-    const int t = tokens(i, &seq, &part, &ctx);
-    if (t > 0) atomicAdd(&hist[kPlanBuckets - 1 - ((t - 1) >> shift)], 1);
+  // Tokens of span slot `slot` (of 2^k partitions) of a sequence; a sequence
+  // with an empty context still owns one item, whose output rows are zeros.
+  auto span_tokens = [&](int c, int k, int slot) {
+    return (slot == 0 && c == 0) ? 1 : min(P << k, c - slot * (P << k));
+  };
+  for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+    const int c = max(0, min(a.context_lens[s], a.ctx_limit));
+    if (s < kPlanCtxCache) s_ctx[s] = c;
+    for (int k = 0; k <= max_k; ++k)
+      for (int slot = 0;; ++slot) {
+        const int t = span_tokens(c, k, slot);
+        if (t <= 0) break;
+        atomicAdd(&hist[k][kPlanBuckets - 1 - ((t - 1) >> shift[k])], 1);
+      }
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int b = 0; b < kPlanBuckets; ++b) {
-      const int c = hist[b];
-      hist[b] = run;
-      run += c;
+  static_assert(kPlanBuckets == kWave, "one bucket per lane of wave 0");
+  if (tid < kWave) {
+    // Wave 0, one bucket per lane: item counts per span, then the exclusive
+    // prefix sum of the chosen span's histogram (the bucket offsets).
+    int k_use = 0;
+    for (int k = max_k; k >= 1; --k) {
+      int items = hist[k][tid];
+      for (int off = 1; off < kWave; off <<= 1) items += __shfl_xor(items, off, kWave);
+      if (items >= a.plan_min_items) {
+        k_use = k;
+        break;
+      }
     }
-    *a.plan_count = run;
+    const int c = hist[k_use][tid];
+    int incl = c;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(incl, off, kWave);
+      if (tid >= off) incl += v;
+    }
+    hist[k_use][tid] = incl - c;
+    if (tid == kWave - 1) {
+      *a.plan_count = incl;
+      s_span = k_use;
+    }
   }
   __syncthreads();
-  for (int64_t i = tid; i < n; i += kPlanThreads) {
-    int seq, part, ctx;
-    const int t = tokens(i, &seq, &part, &ctx);
-    if (t <= 0) continue;
-    const int pos = atomicAdd(&hist[kPlanBuckets - 1 - ((t - 1) >> shift)], 1);
-    a.plan[pos] = make_int4(seq, part, 1, ctx);
+  const int k = s_span;
+  const int span = 1 << k;
+  for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+    const int c = ctx_of(s);
+    const int single = c <= P ? 1 : 0;  // one partition: the output is final
+    for (int slot = 0;; ++slot) {
+      const int t = span_tokens(c, k, slot);
+      if (t <= 0) break;
+      const int pos = atomicAdd(&hist[k][kPlanBuckets - 1 - ((t - 1) >> shift[k])], 1);
+      a.plan[pos] = make_int4(s, slot * span, span | (single << 8), c);
+    }
   }
 }
 
@@ -392,14 +432,22 @@ DecodeWorkspace decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int
   return w;
 }
 
-hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_seqs <= 0) return hipSuccess;
+hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) {
+  if (args.num_seqs <= 0) return hipSuccess;
+  DecodeArgs a = args;
+  const bool mfma = a.dtype != PA_DTYPE_F32;
+  a.plan_min_items = 0;
+  if (mfma) {
+    // Join partitions while every persistent workgroup still gets two units.
+    const int group = a.num_heads / a.num_kv_heads;
+    const int per = a.num_kv_heads * ((group + 15) / 16);
+    a.plan_min_items = std::max(1, (2 * decode_mfma_grid(a) + per - 1) / per);
+  }
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.dtype == PA_DTYPE_F32) return launch_partitions_e<F32>(a, stream);
-  if (a.num_heads / a.num_kv_heads >= kMfmaMinGroup) return launch_decode_mfma(a, stream);
-  return launch_decode_rows(a, stream);
+  if (mfma) return launch_decode_mfma(a, stream);
+  return launch_partitions_e<F32>(a, stream);
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {

@@ -132,7 +132,9 @@ __device__ inline T scalar_ptr(const void* p) {
 struct Unit {
   bool valid;
   int seq, kvh, h_first, nh;
-  int tb, te, ctx;  // token range [tb, te) of the partition; context length
+  int tb, te, ctx;  // token range [tb, te) of the item; context length
+  int span;         // partitions joined in the item (its state goes to the first)
+  bool single;      // the sequence has one partition: write the output directly
   int mine;         // passes of this wave (passes w, w + 4, ... of the unit)
 };
 
@@ -183,13 +185,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     const int j = x.valid ? uu / per : 0;
     const int r = x.valid ? uu - j * per : 0;
     x.seq = plan[4 * static_cast<int64_t>(j)];
+    const int span_word = plan[4 * static_cast<int64_t>(j) + 2];
     x.ctx = plan[4 * static_cast<int64_t>(j) + 3];
+    x.span = span_word & 0xff;
+    x.single = (span_word >> 8) & 1;
     x.kvh = r / head_chunks;
     const int chunk = r - x.kvh * head_chunks;
     x.h_first = x.kvh * group + chunk * kHeadTile;
     x.nh = min(kHeadTile, group - chunk * kHeadTile);
     x.tb = plan[4 * static_cast<int64_t>(j) + 1] * P;
-    x.te = min(x.tb + P, x.ctx);
+    x.te = min(x.tb + x.span * P, x.ctx);
     const int npass = (x.valid && x.te > x.tb) ? (x.te - x.tb + kTile - 1) / kTile : 0;
     x.mine = npass > wave ? (npass - wave + kWaves - 1) / kWaves : 0;
     return x;
@@ -321,6 +326,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     __syncthreads();
     const int nparts = max(1, (x.ctx + P - 1) / P);
     const int part = x.tb / P;
+    const int part_end = min(part + x.span, nparts);
     // Four consecutive dims of one head per thread and step.
     constexpr int D4 = D / 4;
     for (int idx = tid; idx < x.nh * D4; idx += kDecodeThreads) {
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
                        reinterpret_cast<const float*>(&s_kv[w][s_part[w]][0][0][0]) + h * D + d);
       }
       const int64_t row = static_cast<int64_t>(x.seq) * a.num_heads + x.h_first + h;
-      if (nparts == 1) {
+      if (x.single) {
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
         if (den != 0.f) o = num / den;
         const u32x2 packed = {M::pack(o[0], o[1]), M::pack(o[2], o[3])};
@@ -355,6 +361,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
         if (d == 0) {
           a.ws_max[ws] = mx;
           a.ws_sum[ws] = den;
+          for (int q = part + 1; q < part_end; ++q) {  // joined partitions: empty states
+            a.ws_max[ws + q - part] = -__builtin_inff();
+            a.ws_sum[ws + q - part] = 0.f;
+          }
         }
       }
     }
@@ -449,6 +459,15 @@ int persistent_grid() {
   return g;
 }
 
+template <typename E>
+int grid_e(int head_dim) {
+  switch (head_dim) {
+    case 64: return persistent_grid<E, 64>();
+    case 128: return persistent_grid<E, 128>();
+    default: return persistent_grid<E, 256>();
+  }
+}
+
 template <typename E, int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_heads / a.num_kv_heads;
@@ -472,6 +491,10 @@ hipError_t launch_e(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+int decode_mfma_grid(const DecodeArgs& a) {
+  return a.dtype == PA_DTYPE_BF16 ? grid_e<BF16>(a.head_dim) : grid_e<F16>(a.head_dim);
+}
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
   if (a.dtype == PA_DTYPE_BF16) return launch_e<BF16>(a, stream);

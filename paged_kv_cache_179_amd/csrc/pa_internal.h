@@ -38,7 +38,7 @@ struct DecodeArgs {
   float* ws_max;   // [S][Hq][P] running max (log2 units)
   float* ws_sum;   // [S][Hq][P] softmax denominators
   float* ws_acc;   // [S][Hq][P][D] un-normalised partial outputs
-  int4* plan;      // [S * P] work items (seq, partition, 1, context length), longest first
+  int4* plan;      // [S * P] work items (seq, first partition, span | single << 8, ctx), longest first
   int32_t* plan_count;  // number of valid items in `plan`
   int32_t num_seqs;
   int32_t num_heads;
@@ -50,6 +50,7 @@ struct DecodeArgs {
   int32_t ctx_limit;       // min(max_context_len, max_blocks_per_seq * block_size)
   int32_t part_tokens;     // tokens per partition (> 0)
   int32_t num_parts;       // partitions covering ctx_limit
+  int32_t plan_min_items;  // the plan may join partitions while it keeps this many items (0: never)
   float scale;
   pa_dtype dtype;
 };
@@ -86,12 +87,10 @@ struct PrefillArgs {
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
-// 16-bit caches, vector kernel (decode_rows.hip): used below kMfmaMinGroup
-// query heads per KV head.
-hipError_t launch_decode_rows(const DecodeArgs& a, hipStream_t stream);
-// 16-bit caches, grouped-query heads on MFMA (decode_mfma.hip).
+// 16-bit caches: the MFMA kernel (decode_mfma.hip), any group size.
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
-constexpr int kMfmaMinGroup = 2;
+// Workgroups one launch of the MFMA kernel keeps resident (its persistent grid).
+int decode_mfma_grid(const DecodeArgs& a);
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 struct PrefillWorkspace {
   size_t bytes;

@@ -87,6 +87,27 @@ def test_decode_small(gpu, case, partition_size):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("case", [("bf16", 16, 2, 64), ("fp16", 4, 4, 128), ("bf16", 2, 2, 256)],
+                         ids=["bf16-h16x2-d64", "fp16-h4x4-d128", "bf16-h2x2-d256"])
+def test_decode_joined_partitions(gpu, case):
+    """Enough short partitions (64 tokens) that the work plan joins 2 or 4 of
+    them per work item: the joined partitions carry empty states that the
+    reduce must skip.  Every output row is compared."""
+    dtype, hq, hkv, d_ = case
+    say(f"decode joined partitions {case}")
+    w = W.small_case(300 + hq + d_, num_seqs=512, ctx_lo=1, ctx_hi=700, num_heads=hq,
+                     num_kv_heads=hkv, head_dim=d_, block_size=16, dtype=dtype,
+                     extra_ctx=[64, 65, 128, 255, 256, 257, 1])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    out = run_decode(w, d, 64)
+    torch.cuda.synchronize()
+    kc, vc = written_caches(w)
+    err = max_err(out, oracle_decode(w, kc, vc))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 def test_cache_write_bit_exact(gpu, dtype):
     w = W.small_case(7, num_seqs=9, ctx_lo=1, ctx_hi=200, num_heads=8, num_kv_heads=4,
