@@ -294,10 +294,10 @@ def _cpu_model():
 # ---------------------------------------------------------------------------
 def partition_kernel_name(w):
     """Symbol of the decode partition kernel that serves workload w."""
-    g = w.num_heads // w.num_kv_heads
     if w.dtype == "fp32":
-        return f"decode_partition_kernel<F32,{w.head_dim},...>"
-    return f"decode_rows_kernel<{w.dtype.upper().replace('FP', 'F')},{w.head_dim},{g}>"
+        g = min(8, w.num_heads // w.num_kv_heads)
+        return f"decode_partition_kernel<F32,{w.head_dim},{g}>"
+    return f"decode_mfma_kernel<{w.dtype.upper().replace('FP', 'F')},{w.head_dim}>"
 
 
 def kernel_source_hash():
