@@ -32,11 +32,12 @@ HIPCC_FLAGS = [
     f"-I{REPO / 'include'}",
     f"-I{CSRC}",
 ]
-# Per-source extras.  The MFMA decode kernel rescales its accumulators with
+# Per-source extras.  The MFMA kernels rescale their accumulators with
 # vector ALU ops inside the loop; keeping MFMA results in ordinary VGPRs (not
 # AGPRs) avoids a copy of every accumulator in and out on each pass.
 EXTRA_FLAGS = {
     "decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -7,27 +7,37 @@
 // other requests' decode); the GQA mapping is the mini-vLLM one (each query
 // head reads its own KV head).
 //
-// Unlike decode, a tile of query rows makes both products dense, so they run
-// on the matrix cores (v_mfma_f32_32x32x16_{bf16,f16}, fp32 accumulate):
+// A tile of query rows makes both products dense, so both run on the matrix
+// cores (v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulate):
 //
 // * A workgroup is 4 waves x 32 query rows.  Rows are (position, head) pairs of
 //   one KV head, head-minor, so the G query heads that share a KV head share
-//   every K/V tile that is staged (for MQA, 16 positions x 8 heads).
-// * Scores are computed transposed, S^T = K Q^T (keys x rows), so that each
-//   lane of the accumulator holds one query row: the row max and sum of the
-//   online softmax stay inside a lane apart from one exchange between the two
-//   half-waves, and rescaling the output is a per-lane multiply.
-// * O^T += V^T P^T.  P^T comes straight from the score accumulator registers
-//   (exp2, rounded to the input type); V is staged transposed in LDS
-//   ([dim][key]) so its operand is two 8-byte LDS reads per MFMA.
-// * The keys of a tile are split in ranges of kSplitKeys so that long contexts
+//   every K/V tile (for MQA, 16 positions x 8 heads).  A wave's 32 rows are two
+//   16-row MFMA tiles; their query rows stay in registers.
+// * Keys go by passes of 32.  Each pass's K and V rows are copied HBM -> LDS by
+//   the gfx950 global-to-LDS DMA, a quarter of the rows by each wave, into one
+//   of two or three buffers: the next passes are in flight while one is
+//   computed.
+//   Rows are stored with their 16-byte chunks rotated (K by the row, V by twice
+//   the row) so that the compute reads below are bank-conflict free.
+// * Scores, transposed: S^T = K Q^T (keys x rows).  Lane l of the accumulator
+//   holds row l % 16's scores of keys 4 (l / 16) + 0..3 of each 16-key half,
+//   so the row max of the online softmax is one in-lane max and two lane swaps.
+// * O^T += V^T P^T with the 32 keys of the pass as the contraction: the score
+//   registers (exp2, rounded to the input type) are already P^T's operand once
+//   the key order inside the pass is taken as (first half's 4 keys, second
+//   half's 4 keys) per lane; V^T's operand, in the same key order, comes from
+//   two transposing LDS reads (ds_read_b64_tr_b16).  One more MFMA against a
+//   ones operand sums the rounded probabilities (the softmax denominator).
+// * The keys of a chunk are split in ranges of kSplitKeys so that long contexts
 //   spread over several workgroups; each range writes an (m, l, acc) partial
 //   per row and prefill_merge combines them by log-sum-exp weights, as the
 //   decode reduce does.  Rows whose keys fit one range are written directly.
 //
 // Scores are kept in log2 units (scale * log2 e folded in): one v_exp_f32 per
-// probability.
+// probability.  The running max is only moved when a score passes it by 2^8.
 #include "device_common.h"
+#include "lds_dma.h"
 #include "pa_internal.h"
 
 namespace pa {
@@ -35,49 +45,55 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerWg = 4 * kRowsPerWave;
-constexpr int kKeyTile = 32;
+constexpr int kRowsPerWg = kWaves * kRowsPerWave;
+constexpr int kKeyTile = 32;  // keys per pass
 constexpr int kSplitKeys = 1024;
+constexpr float kLazyMax = 8.f;
 
 template <typename E>
-struct Mfma;
+struct Mma;
 template <>
-struct Mfma<BF16> {
-  __device__ static inline f32x16 run(const u32x4& a, const u32x4& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+struct Mma<BF16> {
+  static constexpr unsigned kOnePair = 0x3F803F80u;
+  __device__ static inline f32x4 run(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
-  // Round to bf16 (nearest-even); returns the 16-bit pattern.
-  __device__ static inline unsigned short round_bits(float x) {
-    return __builtin_bit_cast(unsigned short, static_cast<__bf16>(x));
-  }
-  __device__ static inline float from_bits(unsigned short b) {
-    return __uint_as_float(static_cast<unsigned>(b) << 16);
+  __device__ static inline unsigned pack(float lo, float hi) {
+    const bf16x2 r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(unsigned, r);
   }
 };
 template <>
-struct Mfma<F16> {
-  __device__ static inline f32x16 run(const u32x4& a, const u32x4& b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+struct Mma<F16> {
+  static constexpr unsigned kOnePair = 0x3C003C00u;
+  __device__ static inline f32x4 run(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
-  __device__ static inline unsigned short round_bits(float x) {
-    return __builtin_bit_cast(unsigned short, static_cast<_Float16>(x));
-  }
-  __device__ static inline float from_bits(unsigned short b) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, b));
+  __device__ static inline unsigned pack(float lo, float hi) {
+    const f16x2 r = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
+    return __builtin_bit_cast(unsigned, r);
   }
 };
 
-// Byte-select of v_perm_b32: result byte i = byte sel[i] of {hi:lo}.
-__device__ inline unsigned perm(unsigned hi, unsigned lo, unsigned sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
+// Max over lanes l, l ^ 16, l ^ 32, l ^ 48 (each swap hands a lane its own
+// value and its partner's, in some order).
+__device__ inline float max_across_rows(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
+
+typedef __attribute__((address_space(4))) const int32_t cint;
 
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_t group,
@@ -86,13 +102,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
                                                           uint32_t per_xcd, float scale_log2,
                                                           float* ws_max, float* ws_sum,
                                                           float* ws_acc) {
-  constexpr int KPAD = D + 8;          // K tile row stride (elements)
-  constexpr int VPAD = kKeyTile + 4;   // V^T tile row stride (elements)
-  constexpr int NKS = D / 16;          // k-steps of the score product
-  constexpr int NDB = D / 32;          // 32-wide output column blocks
-  __shared__ __attribute__((aligned(16))) unsigned short s_k[kKeyTile * KPAD];
-  __shared__ __attribute__((aligned(16))) unsigned short s_vt[D * VPAD];
-  __shared__ int32_t s_tbl[kSplitKeys];
+  using M = Mma<E>;
+  constexpr int NC = D / 8;             // 16-byte chunks per row
+  constexpr int RB = 2 * D;             // row bytes
+  constexpr int RPI = 1024 / RB;        // rows per DMA instruction
+  constexpr int WKEYS = kKeyTile / kWaves;  // keys each wave copies per pass
+  static_assert(WKEYS % RPI == 0, "a wave copies whole DMA instructions");
+  constexpr int NDW = 2 * (WKEYS / RPI);    // DMA instructions per wave per pass (K and V)
+  constexpr int KB = D / 32;            // k-steps of the score product
+  constexpr int MT = D / 16;            // 16-dim output tiles
+  // [buffer][K or V][key][chunk]; NBUF - 1 passes in flight ahead of the one
+  // computed.  Two buffers at head_dim 256 keep two workgroups per CU.
+  constexpr int NBUF = D == 256 ? 2 : 3;
+  __shared__ u32x4 s_kv[NBUF][2][kKeyTile][NC];
 
   const uint32_t logical = xcd_remap(blockIdx.x, per_xcd);
   if (logical >= n_logical) return;
@@ -120,180 +142,207 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int l32 = lane & 31;
-  const int half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane & 15;
+  const int g4 = lane >> 4;
 
-  // This lane's query row.
-  const int row = wave * kRowsPerWave + l32;
-  const int rpos = row / group;
-  const int rhead = row - rpos * group;
-  const bool row_ok = rpos < npos;
-  const int row_lim = row_ok ? ctx - qlen + pos0 + rpos : -1;
-  const int hq = kvh * group + rhead;
-  const int64_t q_row = static_cast<int64_t>(q_begin) + pos0 + rpos;
-
-  u32x4 qf[NKS];
-  {
-    const char* qp = static_cast<const char*>(a.query) +
-                     (q_row * a.num_heads + hq) * static_cast<int64_t>(D) * 2;
+  // This lane's two query rows (one per 16-row tile of the wave).
+  int row_lim[2], rpos[2], rhead[2];
+  bool row_ok[2];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = row_ok ? load16(qp + (16 * ks + 8 * half) * 2) : u32x4{0u, 0u, 0u, 0u};
+  for (int t = 0; t < 2; ++t) {
+    const int row = wave * kRowsPerWave + 16 * t + hl;
+    rpos[t] = row / group;
+    rhead[t] = row - rpos[t] * group;
+    row_ok[t] = rpos[t] < npos;
+    row_lim[t] = row_ok[t] ? ctx - qlen + pos0 + rpos[t] : -1;
   }
+  // Last key any row of this wave sees (wave-uniform): passes past it are skipped.
+  const int wave_last = min(last_key, ctx - qlen + pos0 + min(npos - 1, (wave * kRowsPerWave + 31) / group));
 
-  // Block ids of this key range.
+  // B operands of the scores: lane (hl, g4) of tile t holds dims 32 kb + 8 g4 .. + 7.
+  u32x4 q[2][KB];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const char* qp = static_cast<const char*>(a.query) +
+                     ((static_cast<int64_t>(q_begin) + pos0 + (row_ok[t] ? rpos[t] : 0)) * a.num_heads +
+                      kvh * group + rhead[t]) * static_cast<int64_t>(RB);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      q[t][kb] = row_ok[t] ? load16(qp + (32 * kb + 8 * g4) * 2) : u32x4{0u, 0u, 0u, 0u};
+  }
+  wait_vmcnt<0>();  // once, before any DMA: no compiler wait inside the pass loop
+
   const int lbs = a.log2_block_size;
   const int off_mask = (1 << lbs) - 1;
-  const int first_blk = key_lo >> lbs;
-  {
-    const int nblk = ((key_hi - 1) >> lbs) - first_blk + 1;
-    const int32_t* table = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
-    for (int i = tid; i < nblk; i += kThreads) {
-      const int b = table[first_blk + i];
-      s_tbl[i] = (b < 0 || b >= a.num_blocks) ? 0 : b;
-    }
-  }
-
   const char* kbase = static_cast<const char*>(a.key_cache);
   const char* vbase = static_cast<const char*>(a.value_cache);
-  constexpr int64_t kRowBytes = static_cast<int64_t>(D) * 2;
+  const int64_t trow = static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+  cint* tables = reinterpret_cast<cint*>(reinterpret_cast<uintptr_t>(a.block_tables));
 
-  f32x16 o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = -__builtin_inff();
-  float lsum = 0.f;
+  // Rotation (in chunks) of key row r and value row r of a tile.
+  auto rot_k = [](int r) { return r % NC; };
+  auto rot_v = [](int r) { return D == 64 ? (r & ~1) % NC : (2 * r) % NC; };
 
-  for (int k0 = key_lo; k0 < key_hi; k0 += kKeyTile) {
-    __syncthreads();  // the table is staged / the previous tile is consumed
-    // K tile: [key][dim] (16-byte chunks).
-    for (int c = tid; c < kKeyTile * D / 8; c += kThreads) {
-      const int key = c / (D / 8);
-      const int dc = c - key * (D / 8);
-      const int kabs = k0 + key;
-      u32x4 v{0u, 0u, 0u, 0u};
-      if (kabs < key_hi) {
-        const int64_t blk = s_tbl[(kabs >> lbs) - first_blk];
-        v = load16(kbase + ((blk * a.num_kv_heads + kvh) << lbs | (kabs & off_mask)) * kRowBytes +
-                   dc * 16);
-      }
-      *reinterpret_cast<u32x4*>(&s_k[key * KPAD + dc * 8]) = v;
-    }
-    // V tile, transposed: [dim][key], 4 keys x 8 dims per unit.
-    for (int u = tid; u < (kKeyTile / 4) * (D / 8); u += kThreads) {
-      const int kg = u / (D / 8);
-      const int dc = u - kg * (D / 8);
-      u32x4 r[4];
+  // This wave's share of pass `p`'s DMA (keys 8 wave .. 8 wave + 7 of the
+  // pass) into buffer `b`.  Keys past the range are clamped to its last key.
+  auto issue = [&](int p, int b) {
+    const int k0 = key_lo + p * kKeyTile + wave * WKEYS;
+    const char* kd = reinterpret_cast<const char*>(&s_kv[b][0][wave * WKEYS][0]);
+    const char* vd = reinterpret_cast<const char*>(&s_kv[b][1][wave * WKEYS][0]);
+    if (lbs >= 3) {
+      // The wave's 8 keys lie in one block: one scalar table read.
+      int blk = tables[trow + (min(k0, key_hi - 1) >> lbs)];
+      blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+      const int64_t head_off = ((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) * RB;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kabs = k0 + 4 * kg + j;
-        r[j] = u32x4{0u, 0u, 0u, 0u};
-        if (kabs < key_hi) {
-          const int64_t blk = s_tbl[(kabs >> lbs) - first_blk];
-          r[j] = load16(vbase + ((blk * a.num_kv_heads + kvh) << lbs | (kabs & off_mask)) * kRowBytes +
-                        dc * 16);
-        }
+      for (int r = 0; r < WKEYS / RPI; ++r) {
+        const int row = wave * WKEYS + r * RPI + lane / NC;  // row of the tile
+        const int pos = lane % NC;
+        const int key = min(k0 + r * RPI + lane / NC, key_hi - 1);
+        const int64_t roff = head_off + static_cast<int64_t>(key & off_mask) * RB;
+        dma16(kbase + roff + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+        dma16(vbase + roff + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
       }
+    } else {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const u32x2 lo{perm(r[1][w], r[0][w], 0x05040100u), perm(r[3][w], r[2][w], 0x05040100u)};
-        const u32x2 hi{perm(r[1][w], r[0][w], 0x07060302u), perm(r[3][w], r[2][w], 0x07060302u)};
-        *reinterpret_cast<u32x2*>(&s_vt[(dc * 8 + 2 * w) * VPAD + 4 * kg]) = lo;
-        *reinterpret_cast<u32x2*>(&s_vt[(dc * 8 + 2 * w + 1) * VPAD + 4 * kg]) = hi;
+      for (int r = 0; r < WKEYS / RPI; ++r) {
+        const int row = wave * WKEYS + r * RPI + lane / NC;
+        const int pos = lane % NC;
+        const int key = min(k0 + r * RPI + lane / NC, key_hi - 1);
+        int blk = a.block_tables[trow + (key >> lbs)];
+        blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+        const int64_t roff = (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * RB;
+        dma16(kbase + roff + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+        dma16(vbase + roff + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
       }
     }
-    __syncthreads();
+  };
 
-    // S^T (32 keys x 32 rows of this wave).
-    f32x16 st;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) st[r] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const u32x4 ka = *reinterpret_cast<const u32x4*>(&s_k[l32 * KPAD + 16 * ks + 8 * half]);
-      st = Mfma<E>::run(ka, qf[ks], st);
-    }
+  // Per-lane LDS offsets (bytes within one K or V tile), as a row base and a
+  // rotated chunk position; NC is a power of two.
+  //   keys: row 16 h + hl, chunk 4 kb + g4;
+  //   values (transposing reads): row 16 h + 4 g4 + hl / 4, dims 16 mt + 4 (hl % 4).
+  static_assert((NC & (NC - 1)) == 0, "chunk count is a power of two");
+  const int vrow0 = 4 * g4 + (hl >> 2);
+  const int q4 = hl & 3;
+  const int vpos0 = (q4 >> 1) - rot_v(vrow0);  // row 16 + vrow0: rotation + 32, the same mod NC
+  auto koff = [&](int h, int kb) {
+    return (16 * h + hl) * RB + ((g4 - rot_k(16 * h + hl) + 4 * kb) & (NC - 1)) * 16;
+  };
+  auto voff = [&](int h, int mt) {
+    return (16 * h + vrow0) * RB + ((vpos0 + 2 * mt) & (NC - 1)) * 16 + (q4 & 1) * 8;
+  };
 
-    // Online softmax for this lane's row (accumulator register r holds key
-    // 8*(r/4) + 4*half + r%4 of the tile).
-    float s[16];
-    float tmax = -__builtin_inff();
+  const u32x4 ones = {M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair};
+  f32x4 acc[2][MT];
+  f32x4 lacc[2];
+  float m[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      s[r] = (key <= row_lim && key < key_hi) ? st[r] * scale_log2 : -__builtin_inff();
-      tmax = fmaxf(tmax, s[r]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m, tmax);
-    const float mu = safe_max(m_new);
-    const float alpha = exp2_fast(m - mu);
-    m = m_new;
-    lsum *= alpha;
+  for (int t = 0; t < 2; ++t) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-
-    u32x4 pb[2];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const unsigned short b0 = Mfma<E>::round_bits(exp2_fast(s[8 * ks2 + 2 * w] - mu));
-        const unsigned short b1 = Mfma<E>::round_bits(exp2_fast(s[8 * ks2 + 2 * w + 1] - mu));
-        lsum += Mfma<E>::from_bits(b0) + Mfma<E>::from_bits(b1);
-        pb[ks2][w] = static_cast<unsigned>(b0) | (static_cast<unsigned>(b1) << 16);
-      }
-    }
-
-    // O^T (dims x rows) += V^T P^T.
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const unsigned short* vrow = &s_vt[(32 * db + l32) * VPAD + 16 * ks2 + 4 * half];
-        const u32x2 x = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 y = *reinterpret_cast<const u32x2*>(vrow + 8);
-        o[db] = Mfma<E>::run(u32x4{x[0], x[1], y[0], y[1]}, pb[ks2], o[db]);
-      }
-    }
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[t] = -__builtin_inff();
   }
 
-  if (!row_ok || key_lo > row_lim) return;  // no key of this range for this row
-  lsum += __shfl_xor(lsum, 32, 64);
-  const int nsplit_row = (row_lim + kSplitKeys) / kSplitKeys;
-  const int64_t out_row = q_row * a.num_heads + hq;
-  if (nsplit_row == 1) {
-    const float inv = 1.f / lsum;
-    // Output register r of block db holds dim 32*db + 8*(r/4) + 4*half + r%4.
+  auto compute = [&](int p, int b) {
+    const int k0 = key_lo + p * kKeyTile;
+    const char* kt = reinterpret_cast<const char*>(&s_kv[b][0][0][0]);
+    const char* vt = reinterpret_cast<const char*>(&s_kv[b][1][0][0]);
+    // S^T of the pass: s[h][t] holds keys k0 + 16 h + 4 g4 + i of row 16 t + hl.
+    f32x4 s[2][2];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int h = 0; h < 2; ++h) {
+      s[h][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        unsigned short bits[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bits[i] = Mfma<E>::round_bits(o[db][4 * j + i] * inv);
-        const u32x2 pk{static_cast<unsigned>(bits[0]) | (static_cast<unsigned>(bits[1]) << 16),
-                       static_cast<unsigned>(bits[2]) | (static_cast<unsigned>(bits[3]) << 16)};
-        *reinterpret_cast<u32x2*>(static_cast<char*>(a.out) +
-                                  (out_row * D + 32 * db + 8 * j + 4 * half) * 2) = pk;
+      for (int kb = 0; kb < KB; ++kb) {
+        const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + koff(h, kb));
+        s[h][0] = M::run(ka, q[0][kb], s[h][0]);
+        s[h][1] = M::run(ka, q[1][kb], s[h][1]);
       }
-  } else {
-    const int64_t ws = out_row * nsplit + split;
+    }
+    u32x4 pb[2];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int t = 0; t < 2; ++t) {
+      float sc[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<u32x4*>(&ws_acc[ws * D + 32 * db + 8 * j + 4 * half]) =
-            u32x4{__float_as_uint(o[db][4 * j]), __float_as_uint(o[db][4 * j + 1]),
-                  __float_as_uint(o[db][4 * j + 2]), __float_as_uint(o[db][4 * j + 3])};
-    if (half == 0) {
-      ws_max[ws] = m;
-      ws_sum[ws] = lsum;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = k0 + 16 * h + 4 * g4 + i;
+          sc[4 * h + i] = (key <= row_lim[t] && key < key_hi) ? s[h][t][i] * scale_log2 : -__builtin_inff();
+        }
+      float mx = sc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+      mx = max_across_rows(mx);
+      if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyMax) != 0) {  // wave-uniform
+        const float m_new = fmaxf(m[t], mx);
+        const float alpha = exp2_fast(m[t] - safe_max(m_new));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] *= alpha;
+        lacc[t] *= alpha;
+        m[t] = m_new;
+      }
+      const float mu = safe_max(m[t]);
+      pb[t] = u32x4{M::pack(exp2_fast(sc[0] - mu), exp2_fast(sc[1] - mu)),
+                    M::pack(exp2_fast(sc[2] - mu), exp2_fast(sc[3] - mu)),
+                    M::pack(exp2_fast(sc[4] - mu), exp2_fast(sc[5] - mu)),
+                    M::pack(exp2_fast(sc[6] - mu), exp2_fast(sc[7] - mu))};
+      lacc[t] = M::run(ones, pb[t], lacc[t]);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const u32x2 v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(0, mt))));
+      const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(1, mt))));
+      const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+      acc[0][mt] = M::run(va, pb[0], acc[0][mt]);
+      acc[1][mt] = M::run(va, pb[1], acc[1][mt]);
+    }
+  };
+
+  const int npass = (key_hi - key_lo + kKeyTile - 1) / kKeyTile;
+  for (int p = 0; p < NBUF - 1 && p < npass; ++p) issue(p, p);
+  for (int p = 0; p < npass; ++p) {
+    __syncthreads();  // every wave is done with pass p - 1's buffer
+    if (p + NBUF - 1 < npass) issue(p + NBUF - 1, (p + NBUF - 1) % NBUF);
+    // Wait for this wave's share of pass p: the passes issued after it may stay in flight.
+    switch (min(NBUF - 1, npass - 1 - p)) {
+      case 2: wait_vmcnt<2 * NDW>(); break;
+      case 1: wait_vmcnt<NDW>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
+    __syncthreads();  // every wave's share of pass p has landed
+    if (key_lo + p * kKeyTile <= wave_last) compute(p, p % NBUF);  // wave-uniform causal skip
+  }
+
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (!row_ok[t] || key_lo > row_lim[t]) continue;  // no key of this range for this row
+    const float lsum = lacc[t][0];
+    const int nsplit_row = (row_lim[t] + kSplitKeys) / kSplitKeys;
+    const int64_t out_row = (static_cast<int64_t>(q_begin) + pos0 + rpos[t]) * a.num_heads + kvh * group + rhead[t];
+    // Output register i of tile mt holds dim 16 mt + 4 g4 + i.
+    if (nsplit_row == 1) {
+      const float inv = 1.f / lsum;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const f32x4 o = acc[t][mt] * inv;
+        const u32x2 packed = {M::pack(o[0], o[1]), M::pack(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(static_cast<char*>(a.out) + (out_row * D + 16 * mt + 4 * g4) * 2) = packed;
+      }
+    } else {
+      const int64_t ws = out_row * nsplit + split;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<f32x4*>(&ws_acc[ws * D + 16 * mt + 4 * g4]) = acc[t][mt];
+      if (g4 == 0) {
+        ws_max[ws] = m[t];
+        ws_sum[ws] = lsum;
+      }
     }
   }
 }
