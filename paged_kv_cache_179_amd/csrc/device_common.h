@@ -125,9 +125,4 @@ __device__ inline float safe_max(float m) { return m == -__builtin_inff() ? 0.f 
 
 __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
 
-// Workgroup index -> logical work index such that each of the 8 XCDs (which
-// receive workgroups round-robin) processes one contiguous range of the
-// logical order.  `per` = ceil(n / 8); the grid has 8 * per workgroups.
-__device__ inline uint32_t xcd_remap(uint32_t b, uint32_t per) { return (b & 7u) * per + (b >> 3); }
-
 }  // namespace pa

@@ -243,12 +243,12 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
 size_t pa_prefill_workspace_bytes(int32_t num_q_tokens, int32_t num_seqs, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
                                   int32_t max_context_len) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  (void)max_query_len;
-  if (num_q_tokens <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  if (num_q_tokens <= 0 || num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+      num_heads % num_kv_heads != 0 || head_dim <= 0 || max_query_len <= 0 || max_context_len <= 0)
+    return 0;
   return pa::prefill_workspace_layout(num_q_tokens, num_heads, head_dim,
-                                      pa::prefill_num_splits(max_context_len))
+                                      pa::prefill_num_splits(max_context_len), num_seqs,
+                                      pa::prefill_num_tiles(num_heads, num_kv_heads, max_query_len))
       .bytes;
 }
 
@@ -277,7 +277,8 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
       std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size));
   if (ctx_limit == 0) return PA_OK;
   const pa::PrefillWorkspace w = pa::prefill_workspace_layout(
-      num_q_tokens, num_heads, head_dim, pa::prefill_num_splits(ctx_limit));
+      num_q_tokens, num_heads, head_dim, pa::prefill_num_splits(ctx_limit), num_seqs,
+      pa::prefill_num_tiles(num_heads, num_kv_heads, max_query_len));
   st = check_workspace(w.bytes, workspace, workspace_bytes);
   if (st != PA_OK) return st;
   pa::PrefillArgs a{};

@@ -94,11 +94,14 @@ int decode_mfma_grid(const DecodeArgs& a);
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream);
 struct PrefillWorkspace {
   size_t bytes;
-  size_t off_max, off_sum, off_acc;
+  size_t off_max, off_sum, off_acc;  // key-range partial states (only when nsplit > 1)
+  size_t off_count, off_plan;        // work plan (always)
 };
 int32_t prefill_num_splits(int32_t ctx_limit);
+int32_t prefill_num_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_query_len);
 PrefillWorkspace prefill_workspace_layout(int32_t num_q_tokens, int32_t num_heads,
-                                          int32_t head_dim, int32_t nsplit);
+                                          int32_t head_dim, int32_t nsplit, int32_t num_seqs,
+                                          int32_t ntiles);
 hipError_t launch_prefill(const PrefillArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace pa

@@ -95,13 +95,86 @@ __device__ inline float max_across_rows(float x) {
 
 typedef __attribute__((address_space(4))) const int32_t cint;
 
+// The chunk, row tile and key range of one item, and the keys its rows see.
+struct PrefillItem {
+  int q_begin, qlen, ctx, pos0, npos, last_key, key_lo, key_hi;
+  bool valid;
+};
+
+__device__ inline PrefillItem prefill_item(const PrefillArgs& a, int seq, int tile, int split,
+                                           int pos_per_tile) {
+  PrefillItem it{};
+  it.q_begin = min(max(a.query_start_loc[seq], 0), a.num_q_tokens);
+  const int q_end = min(max(a.query_start_loc[seq + 1], it.q_begin), a.num_q_tokens);
+  it.ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
+  it.qlen = min(q_end - it.q_begin, it.ctx);
+  it.pos0 = tile * pos_per_tile;
+  it.valid = it.qlen > 0 && it.pos0 < it.qlen;
+  if (!it.valid) return it;
+  it.npos = min(pos_per_tile, it.qlen - it.pos0);
+  it.last_key = it.ctx - it.qlen + it.pos0 + it.npos - 1;  // last key any row of the tile sees
+  it.key_lo = split * kSplitKeys;
+  it.valid = it.key_lo <= it.last_key;
+  it.key_hi = min(it.key_lo + kSplitKeys, it.last_key + 1);
+  return it;
+}
+
+// Work plan of one prefill call: every (chunk, row tile, key range) item that
+// has keys, longest key range first (a counting sort over 64 classes), so the
+// dispatcher starts the long items first and fills the tail with short ones.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = 64;
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs a, int32_t pos_per_tile,
+                                                                   int32_t ntiles, int32_t nsplit,
+                                                                   int4* plan, int32_t* plan_count) {
+  __shared__ int hist[kPlanBuckets];
+  const int tid = threadIdx.x;
+  if (tid < kPlanBuckets) hist[tid] = 0;
+  __syncthreads();
+  static_assert((kSplitKeys - 1) >> 4 < kPlanBuckets, "one class per 16 keys");
+  const int64_t n = static_cast<int64_t>(a.num_seqs) * ntiles * nsplit;
+  auto keys = [&](int64_t i, int* seq, int* tile, int* split) {
+    *split = static_cast<int>(i % nsplit);
+    const int64_t r = i / nsplit;
+    *tile = static_cast<int>(r % ntiles);
+    *seq = static_cast<int>(r / ntiles);
+    const PrefillItem it = prefill_item(a, *seq, *tile, *split, pos_per_tile);
+    return it.valid ? it.key_hi - it.key_lo : 0;
+  };
+  for (int64_t i = tid; i < n; i += kPlanThreads) {
+    int seq, tile, split;
+    const int t = keys(i, &seq, &tile, &split);
+    if (t > 0) atomicAdd(&hist[kPlanBuckets - 1 - ((t - 1) >> 4)], 1);
+  }
+  __syncthreads();
+  static_assert(kPlanBuckets == kWave, "one class per lane of wave 0");
+  if (tid < kWave) {
+    const int c = hist[tid];
+    int incl = c;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int v = __shfl_up(incl, off, kWave);
+      if (tid >= off) incl += v;
+    }
+    hist[tid] = incl - c;
+    if (tid == kWave - 1) *plan_count = incl;
+  }
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += kPlanThreads) {
+    int seq, tile, split;
+    const int t = keys(i, &seq, &tile, &split);
+    if (t <= 0) continue;
+    const int pos = atomicAdd(&hist[kPlanBuckets - 1 - ((t - 1) >> 4)], 1);
+    plan[pos] = make_int4(seq, tile, split, t);
+  }
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_t group,
-                                                          int32_t pos_per_tile, int32_t ntiles,
-                                                          int32_t nsplit, uint32_t n_logical,
-                                                          uint32_t per_xcd, float scale_log2,
-                                                          float* ws_max, float* ws_sum,
-                                                          float* ws_acc) {
+                                                          int32_t pos_per_tile, int32_t nsplit,
+                                                          const int4* plan, const int32_t* plan_count,
+                                                          float scale_log2, float* ws_max,
+                                                          float* ws_sum, float* ws_acc) {
   using M = Mma<E>;
   constexpr int NC = D / 8;             // 16-byte chunks per row
   constexpr int RB = 2 * D;             // row bytes
@@ -116,29 +189,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
   constexpr int NBUF = D == 256 ? 2 : 3;
   __shared__ u32x4 s_kv[NBUF][2][kKeyTile][NC];
 
-  const uint32_t logical = xcd_remap(blockIdx.x, per_xcd);
-  if (logical >= n_logical) return;
-  // Logical order ((seq * Hkv + kv_head) * nsplit + split) * ntiles + tile,
-  // with tiles from the end of the chunk (most keys) first.
-  uint32_t rem = logical;
-  const int tile = ntiles - 1 - static_cast<int>(rem % ntiles);
-  rem /= ntiles;
-  const int split = rem % nsplit;
-  rem /= nsplit;
-  const int kvh = rem % a.num_kv_heads;
-  const int seq = rem / a.num_kv_heads;
-
-  const int q_begin = min(max(a.query_start_loc[seq], 0), a.num_q_tokens);
-  const int q_end = min(max(a.query_start_loc[seq + 1], q_begin), a.num_q_tokens);
-  const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
-  const int qlen = min(q_end - q_begin, ctx);
-  const int pos0 = tile * pos_per_tile;
-  if (qlen <= 0 || pos0 >= qlen) return;
-  const int npos = min(pos_per_tile, qlen - pos0);
-  const int last_key = ctx - qlen + pos0 + npos - 1;  // last key any row of the tile sees
-  const int key_lo = split * kSplitKeys;
-  if (key_lo > last_key) return;
-  const int key_hi = min(key_lo + kSplitKeys, last_key + 1);
+  // Item blockIdx.x / Hkv of the plan (longest first), for KV head blockIdx.x % Hkv.
+  const int j = static_cast<int>(blockIdx.x) / a.num_kv_heads;
+  const int kvh = static_cast<int>(blockIdx.x) - j * a.num_kv_heads;
+  if (j >= *plan_count) return;
+  const int4 pi = plan[j];
+  const int seq = pi.x, split = pi.z;
+  const PrefillItem item = prefill_item(a, seq, pi.y, split, pos_per_tile);
+  if (!item.valid) return;
+  const int q_begin = item.q_begin, ctx = item.ctx, qlen = item.qlen, pos0 = item.pos0;
+  const int npos = item.npos, last_key = item.last_key, key_lo = item.key_lo, key_hi = item.key_hi;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -400,25 +460,27 @@ template <typename E, int D>
 hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* workspace) {
   const int group = a.num_heads / a.num_kv_heads;
   const int pos_per_tile = kRowsPerWg / group;
-  const int ntiles = (a.max_query_len + pos_per_tile - 1) / pos_per_tile;
-  const int nsplit = (a.ctx_limit + kSplitKeys - 1) / kSplitKeys;
-  const uint64_t n = static_cast<uint64_t>(a.num_seqs) * a.num_kv_heads * (nsplit > 0 ? nsplit : 1) * ntiles;
-  if (n == 0 || nsplit == 0) return hipSuccess;
-  const uint32_t per = static_cast<uint32_t>((n + 7) / 8);
-  float* ws_max = nullptr;
-  float* ws_sum = nullptr;
-  float* ws_acc = nullptr;
-  if (nsplit > 1) {
-    const PrefillWorkspace w = prefill_workspace_layout(a.num_q_tokens, a.num_heads, a.head_dim, nsplit);
-    char* base = static_cast<char*>(workspace);
-    ws_max = reinterpret_cast<float*>(base + w.off_max);
-    ws_sum = reinterpret_cast<float*>(base + w.off_sum);
-    ws_acc = reinterpret_cast<float*>(base + w.off_acc);
-  }
-  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3(per * 8), dim3(kThreads), 0, stream, a, group,
-                     pos_per_tile, ntiles, nsplit, static_cast<uint32_t>(n), per,
-                     a.scale * kLog2e, ws_max, ws_sum, ws_acc);
+  const int ntiles = prefill_num_tiles(a.num_heads, a.num_kv_heads, a.max_query_len);
+  const int nsplit = prefill_num_splits(a.ctx_limit);
+  const uint64_t items = static_cast<uint64_t>(a.num_seqs) * ntiles * nsplit;
+  if (items == 0) return hipSuccess;
+  const uint64_t n = items * a.num_kv_heads;
+  if (n > 0x7fffffffu) return hipErrorInvalidValue;
+  const PrefillWorkspace w = prefill_workspace_layout(a.num_q_tokens, a.num_heads, a.head_dim, nsplit,
+                                                      a.num_seqs, ntiles);
+  char* base = static_cast<char*>(workspace);
+  float* ws_max = nsplit > 1 ? reinterpret_cast<float*>(base + w.off_max) : nullptr;
+  float* ws_sum = nsplit > 1 ? reinterpret_cast<float*>(base + w.off_sum) : nullptr;
+  float* ws_acc = nsplit > 1 ? reinterpret_cast<float*>(base + w.off_acc) : nullptr;
+  int4* plan = reinterpret_cast<int4*>(base + w.off_plan);
+  int32_t* plan_count = reinterpret_cast<int32_t*>(base + w.off_count);
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, pos_per_tile, ntiles,
+                     nsplit, plan, plan_count);
   hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, stream, a,
+                     group, pos_per_tile, nsplit, plan, plan_count, a.scale * kLog2e, ws_max, ws_sum, ws_acc);
+  err = hipGetLastError();
   if (err != hipSuccess || nsplit <= 1) return err;
   const int64_t rows = static_cast<int64_t>(a.num_q_tokens) * a.num_heads;
   if (rows == 0) return hipSuccess;
@@ -442,15 +504,26 @@ static size_t align256p(size_t x) { return (x + 255) & ~static_cast<size_t>(255)
 
 int32_t prefill_num_splits(int32_t ctx_limit) { return (ctx_limit + kSplitKeys - 1) / kSplitKeys; }
 
-PrefillWorkspace prefill_workspace_layout(int32_t num_q_tokens, int32_t num_heads,
-                                          int32_t head_dim, int32_t nsplit) {
+int32_t prefill_num_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_query_len) {
+  const int pos_per_tile = kRowsPerWg / (num_heads / num_kv_heads);
+  return (max_query_len + pos_per_tile - 1) / pos_per_tile;
+}
+
+PrefillWorkspace prefill_workspace_layout(int32_t num_q_tokens, int32_t num_heads, int32_t head_dim,
+                                          int32_t nsplit, int32_t num_seqs, int32_t ntiles) {
   PrefillWorkspace w{};
-  if (nsplit <= 1 || num_q_tokens <= 0) return w;
-  const size_t n = static_cast<size_t>(num_q_tokens) * num_heads * nsplit;
-  w.off_max = 0;
-  w.off_sum = align256p(n * sizeof(float));
-  w.off_acc = w.off_sum + align256p(n * sizeof(float));
-  w.bytes = w.off_acc + align256p(n * head_dim * sizeof(float));
+  if (num_q_tokens <= 0 || num_seqs <= 0 || ntiles <= 0 || nsplit <= 0) return w;
+  size_t off = 0;
+  if (nsplit > 1) {
+    const size_t n = static_cast<size_t>(num_q_tokens) * num_heads * nsplit;
+    w.off_max = 0;
+    w.off_sum = align256p(n * sizeof(float));
+    w.off_acc = w.off_sum + align256p(n * sizeof(float));
+    off = w.off_acc + align256p(n * head_dim * sizeof(float));
+  }
+  w.off_count = off;
+  w.off_plan = off + 256;
+  w.bytes = w.off_plan + align256p(static_cast<size_t>(num_seqs) * ntiles * nsplit * sizeof(int4));
   return w;
 }
 

@@ -128,8 +128,12 @@ def test_workspace_sizes(lib):
     assert f(128, 32, 128, 4096, 512) == expect
     assert f(0, 32, 128, 4096, 512) == 0
     g = lib.pa_prefill_workspace_bytes
-    assert g(2048, 4, 8, 1, 256, 512, 1024) == 0  # one key range
-    assert g(2048, 4, 8, 1, 256, 512, 4096) > 0
+    # One key range: only the work plan, one 16-byte item per (chunk, 16-position tile).
+    assert g(2048, 4, 8, 1, 256, 512, 1024) == 256 + a256(4 * 32 * 16)
+    # Four key ranges: max, sum and D partial floats per (token, head, range), then the plan.
+    n = 2048 * 8 * 4
+    assert g(2048, 4, 8, 1, 256, 512, 4096) == 2 * a256(n * 4) + a256(n * 256 * 4) + 256 + a256(4 * 32 * 4 * 16)
+    assert g(2048, 4, 8, 3, 256, 512, 4096) == 0  # heads not a multiple of KV heads
 
 
 def prefill(lib, out=P, q=P, qsl=P, nq=64, maxq=32, kc=P, vc=P, bt=P, mbps=8, cl=P, s=2, hq=8,
