@@ -10,13 +10,14 @@
 // A tile of query rows makes both products dense, so both run on the matrix
 // cores (v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulate):
 //
-// * A workgroup is 4 waves x 32 query rows.  Rows are (position, head) pairs of
-//   one KV head, head-minor, so the G query heads that share a KV head share
-//   every K/V tile (for MQA, 16 positions x 8 heads).  A wave's 32 rows are two
-//   16-row MFMA tiles; their query rows stay in registers.
+// * A workgroup has 128 query rows: 4 waves x 32 rows (8 waves x 16 rows at
+//   head_dim 256).  Rows are (position, head) pairs of one KV head,
+//   head-minor, so the G query heads that share a KV head share every K/V tile
+//   (for MQA, 16 positions x 8 heads).  A wave's rows are 16-row MFMA tiles;
+//   their query rows stay in registers.
 // * Keys go by passes of 32.  Each pass's K and V rows are copied HBM -> LDS by
 //   the gfx950 global-to-LDS DMA, a quarter of the rows by each wave, into one
-//   of two or three buffers: the next passes are in flight while one is
+//   of three or four buffers: the next passes are in flight while one is
 //   computed.
 //   Rows are stored with their 16-byte chunks rotated (K by the row, V by twice
 //   the row) so that the compute reads below are bank-conflict free.
@@ -49,10 +50,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kRowsPerWave = 32;
-constexpr int kRowsPerWg = kWaves * kRowsPerWave;
+constexpr int kThreads = 256;   // merge and plan kernels
+constexpr int kRowsPerWg = 128;  // query rows sharing each K/V tile
+// 16-row MFMA tiles per wave: two, except at head_dim 256 where one keeps a
+// wave's registers (accumulators 16 x 256 fp32 per tile) low enough for two
+// waves per SIMD; a workgroup then has 8 waves.
+constexpr int prefill_row_tiles(int head_dim) { return head_dim == 256 ? 1 : 2; }
+constexpr int prefill_threads(int head_dim) { return kRowsPerWg / (16 * prefill_row_tiles(head_dim)) * 64; }
 constexpr int kKeyTile = 32;  // keys per pass
 constexpr int kSplitKeys = 1024;
 constexpr float kLazyMax = 8.f;
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
 }
 
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_t group,
+__global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs a, int32_t group,
                                                           int32_t pos_per_tile, int32_t nsplit,
                                                           const int4* plan, const int32_t* plan_count,
                                                           float scale_log2, float* ws_max,
@@ -179,14 +183,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
   constexpr int NC = D / 8;             // 16-byte chunks per row
   constexpr int RB = 2 * D;             // row bytes
   constexpr int RPI = 1024 / RB;        // rows per DMA instruction
-  constexpr int WKEYS = kKeyTile / kWaves;  // keys each wave copies per pass
+  constexpr int NTW = prefill_row_tiles(D);  // row tiles per wave
+  constexpr int WAVES = prefill_threads(D) / 64;
+  constexpr int RPW = 16 * NTW;              // rows per wave
+  constexpr int WKEYS = kKeyTile / WAVES;    // keys each wave copies per pass
   static_assert(WKEYS % RPI == 0, "a wave copies whole DMA instructions");
   constexpr int NDW = 2 * (WKEYS / RPI);    // DMA instructions per wave per pass (K and V)
   constexpr int KB = D / 32;            // k-steps of the score product
   constexpr int MT = D / 16;            // 16-dim output tiles
   // [buffer][K or V][key][chunk]; NBUF - 1 passes in flight ahead of the one
-  // computed.  Two buffers at head_dim 256 keep two workgroups per CU.
-  constexpr int NBUF = D == 256 ? 2 : 3;
+  // computed (at head_dim 256 the 8-wave workgroup has the CU to itself).
+  constexpr int NBUF = D == 256 ? 4 : 3;
   __shared__ u32x4 s_kv[NBUF][2][kKeyTile][NC];
 
   // Item blockIdx.x / Hkv of the plan (longest first), for KV head blockIdx.x % Hkv.
@@ -207,23 +214,23 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
   const int g4 = lane >> 4;
 
   // This lane's two query rows (one per 16-row tile of the wave).
-  int row_lim[2], rpos[2], rhead[2];
-  bool row_ok[2];
+  int row_lim[NTW], rpos[NTW], rhead[NTW];
+  bool row_ok[NTW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = wave * kRowsPerWave + 16 * t + hl;
+  for (int t = 0; t < NTW; ++t) {
+    const int row = wave * RPW + 16 * t + hl;
     rpos[t] = row / group;
     rhead[t] = row - rpos[t] * group;
     row_ok[t] = rpos[t] < npos;
     row_lim[t] = row_ok[t] ? ctx - qlen + pos0 + rpos[t] : -1;
   }
   // Last key any row of this wave sees (wave-uniform): passes past it are skipped.
-  const int wave_last = min(last_key, ctx - qlen + pos0 + min(npos - 1, (wave * kRowsPerWave + 31) / group));
+  const int wave_last = min(last_key, ctx - qlen + pos0 + min(npos - 1, (wave * RPW + RPW - 1) / group));
 
   // B operands of the scores: lane (hl, g4) of tile t holds dims 32 kb + 8 g4 .. + 7.
-  u32x4 q[2][KB];
+  u32x4 q[NTW][KB];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NTW; ++t) {
     const char* qp = static_cast<const char*>(a.query) +
                      ((static_cast<int64_t>(q_begin) + pos0 + (row_ok[t] ? rpos[t] : 0)) * a.num_heads +
                       kvh * group + rhead[t]) * static_cast<int64_t>(RB);
@@ -250,8 +257,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
     const int k0 = key_lo + p * kKeyTile + wave * WKEYS;
     const char* kd = reinterpret_cast<const char*>(&s_kv[b][0][wave * WKEYS][0]);
     const char* vd = reinterpret_cast<const char*>(&s_kv[b][1][wave * WKEYS][0]);
-    if (lbs >= 3) {
-      // The wave's 8 keys lie in one block: one scalar table read.
+    if ((1 << lbs) >= WKEYS) {
+      // The wave's keys lie in one block: one scalar table read.
       int blk = tables[trow + (min(k0, key_hi - 1) >> lbs)];
       blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
       const int64_t head_off = ((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) * RB;
@@ -295,11 +302,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
   };
 
   const u32x4 ones = {M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair};
-  f32x4 acc[2][MT];
-  f32x4 lacc[2];
-  float m[2];
+  f32x4 acc[NTW][MT];
+  f32x4 lacc[NTW];
+  float m[NTW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NTW; ++t) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -311,21 +318,21 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
     const char* kt = reinterpret_cast<const char*>(&s_kv[b][0][0][0]);
     const char* vt = reinterpret_cast<const char*>(&s_kv[b][1][0][0]);
     // S^T of the pass: s[h][t] holds keys k0 + 16 h + 4 g4 + i of row 16 t + hl.
-    f32x4 s[2][2];
+    f32x4 s[2][NTW];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      s[h][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-      s[h][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) s[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + koff(h, kb));
-        s[h][0] = M::run(ka, q[0][kb], s[h][0]);
-        s[h][1] = M::run(ka, q[1][kb], s[h][1]);
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) s[h][t] = M::run(ka, q[t][kb], s[h][t]);
       }
     }
-    u32x4 pb[2];
+    u32x4 pb[NTW];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < NTW; ++t) {
       float sc[8];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -359,8 +366,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
       const u32x2 v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(0, mt))));
       const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(1, mt))));
       const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
-      acc[0][mt] = M::run(va, pb[0], acc[0][mt]);
-      acc[1][mt] = M::run(va, pb[1], acc[1][mt]);
+#pragma unroll
+      for (int t = 0; t < NTW; ++t) acc[t][mt] = M::run(va, pb[t], acc[t][mt]);
     }
   };
 
@@ -371,6 +378,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
     if (p + NBUF - 1 < npass) issue(p + NBUF - 1, (p + NBUF - 1) % NBUF);
     // Wait for this wave's share of pass p: the passes issued after it may stay in flight.
     switch (min(NBUF - 1, npass - 1 - p)) {
+      case 3: wait_vmcnt<3 * NDW>(); break;
       case 2: wait_vmcnt<2 * NDW>(); break;
       case 1: wait_vmcnt<NDW>(); break;
       default: wait_vmcnt<0>(); break;
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a, int32_
   }
 
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < NTW; ++t) {
     if (!row_ok[t] || key_lo > row_lim[t]) continue;  // no key of this range for this row
     const float lsum = lacc[t][0];
     const int nsplit_row = (row_lim[t] + kSplitKeys) / kSplitKeys;
@@ -478,7 +486,7 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
                      nsplit, plan, plan_count);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3(static_cast<uint32_t>(n)), dim3(kThreads), 0, stream, a,
+  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3(static_cast<uint32_t>(n)), dim3(prefill_threads(D)), 0, stream, a,
                      group, pos_per_tile, nsplit, plan, plan_count, a.scale * kLog2e, ws_max, ws_sum, ws_acc);
   err = hipGetLastError();
   if (err != hipSuccess || nsplit <= 1) return err;
