@@ -352,6 +352,53 @@ def copy_probe(nbytes=1 << 30, launches=3):
     log(f"copied {nbytes} bytes x {launches}")
 
 
+def block_ops(dev, reps=10):
+    """Block-pool copies on Llama-2-7B-like blocks (32 KV heads x 16 tokens x
+    128 dims, fp16: 128 KiB per block and pool): copy-on-write of 1024 blocks
+    inside a 4096-block pool (K and V), and a swap of 256 blocks to a pinned
+    host pool and back.  Bytes count each copied byte once read and once
+    written."""
+    import paged_kv_cache_179_amd as pa
+
+    g = torch.Generator(device="cpu").manual_seed(7)
+    nb, hkv, bs, d = 4096, 32, 16, 128
+    kc = torch.randn((nb, hkv, bs, d), generator=g, dtype=torch.float32).to(torch.float16).to(dev)
+    vc = torch.randn((nb, hkv, bs, d), generator=g, dtype=torch.float32).to(torch.float16).to(dev)
+    ids = torch.randperm(nb, generator=g)
+    pairs = torch.stack([ids[:1024], ids[1024:2048]], dim=1).to(torch.int64).to(dev)
+    block = hkv * bs * d * 2
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        ts = []
+        for i in range(reps + 2):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1))
+        return float(np.mean(ts))
+
+    ms_copy = timed(lambda: pa.copy_blocks(kc, vc, pairs))
+    host = torch.empty((512, hkv, bs, d), dtype=torch.float16).pin_memory()
+    out_pairs = torch.stack([ids[:256], torch.arange(256)], dim=1).to(torch.int64).to(dev)
+    in_pairs = torch.stack([torch.arange(256), ids[2048:2304]], dim=1).to(torch.int64).to(dev)
+    ms_out = timed(lambda: pa.swap_blocks(kc, host, out_pairs))
+    ms_in = timed(lambda: pa.swap_blocks(host, kc, in_pairs))
+    copy_bytes = 2 * 2 * 1024 * block
+    swap_bytes = 256 * block
+    return {"copy_blocks": {"pairs": 1024, "block_bytes": block, "ms": round(ms_copy, 5),
+                            "gbs": copy_bytes / (ms_copy * 1e-3) / 1e9,
+                            "hbm_frac": copy_bytes / (ms_copy * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "swap_out_to_pinned_host": {"pairs": 256, "ms": round(ms_out, 5),
+                                        "gbs_one_way": swap_bytes / (ms_out * 1e-3) / 1e9},
+            "swap_in_from_pinned_host": {"pairs": 256, "ms": round(ms_in, 5),
+                                         "gbs_one_way": swap_bytes / (ms_in * 1e-3) / 1e9}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -413,6 +460,10 @@ def main():
         del st
         torch.cuda.empty_cache()
 
+    extras = {}
+    if not args.only:
+        extras = block_ops(dev)
+        log("block ops: " + json.dumps(extras))
     w, wk, t, r = headline
     part_ms = float(np.mean(t["partitions"]))
     achieved = wk["partition_kernel_bytes"] / (part_ms * 1e-3) / 1e9
@@ -444,6 +495,7 @@ def main():
                      "algorithmic_bytes_per_launch": wk["partition_kernel_bytes"]},
         "cpu_baseline": results.get("_cpu"),
         "workloads": {k: v for k, v in results.items() if not k.startswith("_")},
+        "block_ops": extras or None,
     }
     print(json.dumps(line), flush=True)
 

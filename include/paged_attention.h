@@ -17,10 +17,14 @@
  *                         it and itself causally (wLLM PyPI page, "Features --
  *                         Core engine": chunked prefill).
  *
+ * Two block-pool operations sit beside them: pa_copy_blocks (copy-on-write of
+ * a shared block) and pa_swap_blocks (blocks to and from a host pool).
+ *
  * Conventions shared by every call
  * --------------------------------
- * - All array arguments are DEVICE pointers into memory the caller owns; the
- *   library allocates nothing and keeps no state between calls.  Every call
+ * - All array arguments are DEVICE pointers into memory the caller owns
+ *   (pa_swap_blocks also takes pinned host pools); the library allocates
+ *   nothing and keeps no state between calls.  Every call
  *   only enqueues work on `stream` (a hipStream_t; NULL = the null stream) and
  *   returns; results are ready when the stream reaches that point.
  * - Element type `dtype` is shared by query, key/value, caches and output.
@@ -90,10 +94,51 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
                                void* stream);
 
 /*
- * Workspace bytes pa_decode needs: 0 when no sequence can span more than one
- * partition (partition_size == 0 or max_context_len <= partition_size), else
- * num_seqs * num_heads * ceil(max_context_len / partition_size) partial
- * results of (head_dim + 2) floats, each array 256-byte aligned.
+ * Block copy inside one pool, for copy-on-write of a block that several
+ * block tables share (wLLM case study, ADR-001 on the KV-cache layout: prefix
+ * sharing is a block-table operation; mini-vLLM README, "Limitations": block
+ * reference counts are kept for prefix caching).  For every pair
+ * i < num_pairs with (src, dst) = (block_mapping[2i], block_mapping[2i+1]):
+ * key_cache[dst] = key_cache[src] and value_cache[dst] = value_cache[src],
+ * whole blocks ([num_kv_heads][block_size][head_dim] each).  A bit copy.
+ *   key_cache, value_cache  [num_blocks][num_kv_heads][block_size][head_dim]
+ *   block_mapping           int64 [num_pairs][2], device-addressable memory
+ * A pair with an id outside [0, num_blocks) is skipped.  Destinations must be
+ * distinct and no destination may be another pair's source (the pairs run in
+ * no particular order).  num_pairs == 0 is a valid no-op.
+ */
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * Block copy between two pools of the same block size, for swapping a
+ * preempted sequence's blocks out to host memory and back (wLLM PyPI page,
+ * "Features -- Core engine": CPU-swap preemption).  For every pair i:
+ * dst_cache block block_mapping[2i+1] = src_cache block block_mapping[2i],
+ * block_bytes bytes each.  Call it once per pool (K, then V).
+ *   src_cache, dst_cache  [src_num_blocks] and [dst_num_blocks] blocks of
+ *                         block_bytes; either may be host memory that the
+ *                         device can address (pinned: hipHostMalloc, or
+ *                         torch's pin_memory), the other device memory
+ *   block_mapping         int64 [num_pairs][2], device-addressable memory
+ *   block_bytes           > 0, a multiple of 16
+ * A pair with an id outside its pool is skipped; destinations must be
+ * distinct.  The copy is asynchronous on `stream` like every other call.
+ * Each pointer is checked with hipPointerGetAttributes before the launch:
+ * pageable host memory (or a pointer HIP does not know) gives
+ * PA_ERR_UNSUPPORTED, since the kernel could not read it.
+ */
+pa_status pa_swap_blocks(const void* src_cache, void* dst_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int64_t block_bytes, int32_t src_num_blocks,
+                         int32_t dst_num_blocks, void* stream);
+
+/*
+ * Workspace bytes pa_decode needs (0 only when num_seqs <= 0): the work plan,
+ * 256 + 16 * num_seqs * P bytes with P = ceil(max_context_len /
+ * partition_size) (1 when partition_size == 0 or the context fits one
+ * partition), and, when P > 1, num_seqs * num_heads * P partial results of
+ * (head_dim + 2) floats; each region 256-byte aligned.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size);

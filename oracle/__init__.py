@@ -10,3 +10,4 @@ from .attention import (  # noqa: F401
     query_position,
     reshape_and_cache,
 )
+from .blocks import copy_blocks, swap_blocks  # noqa: F401,E402

@@ -8,6 +8,7 @@ raises if the library is missing -- there is no fallback path.
 """
 from .binding import (  # noqa: F401
     PagedAttentionError,
+    copy_blocks,
     decode,
     decode_partitions,
     decode_reduce,
@@ -17,4 +18,5 @@ from .binding import (  # noqa: F401
     prefill_chunk,
     prefill_workspace_bytes,
     reshape_and_cache,
+    swap_blocks,
 )

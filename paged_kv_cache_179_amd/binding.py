@@ -30,6 +30,10 @@ _SIGNATURES = {
     "pa_version": ([], ctypes.c_int),
     "pa_reshape_and_cache": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _i32, _i32, _i32, _i32,
                               ctypes.c_int, _c_ptr], ctypes.c_int),
+    "pa_copy_blocks": ([_c_ptr, _c_ptr, _c_ptr, _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _c_ptr],
+                       ctypes.c_int),
+    "pa_swap_blocks": ([_c_ptr, _c_ptr, _c_ptr, _i32, ctypes.c_int64, _i32, _i32, _c_ptr],
+                       ctypes.c_int),
     "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32], _size),
     "pa_decode": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32, _i32, _i32,
                    _i32, _i32, _i32, _f32, _i32, _c_ptr, _size, ctypes.c_int, _c_ptr],
@@ -122,6 +126,56 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
         _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
         n, hkv, d, bs, nb, PA_DTYPE[dt], _stream(key_cache))
     _check("pa_reshape_and_cache", st)
+
+
+def _mapping(block_mapping: torch.Tensor) -> int:
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs, 2] (source, destination)")
+    return _dev(block_mapping, "block_mapping", torch.int64)
+
+
+def copy_blocks(key_cache: torch.Tensor, value_cache: torch.Tensor,
+                block_mapping: torch.Tensor) -> None:
+    """Copy whole blocks inside the pool: for each row (src, dst) of
+    ``block_mapping`` (int64 [n, 2] on the GPU), K and V block dst := block src."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    dt = key_cache.dtype
+    n = int(block_mapping.shape[0]) if block_mapping.dim() == 2 else -1
+    st = library().pa_copy_blocks(_dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+                                  _mapping(block_mapping), n, hkv, d, bs, nb, PA_DTYPE[dt],
+                                  _stream(key_cache))
+    _check("pa_copy_blocks", st)
+
+
+def _pool(t: torch.Tensor, name: str) -> int:
+    """A block pool on the GPU, or in pinned host memory the GPU can address."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type == "cpu":
+        if not t.is_pinned():
+            raise ValueError(f"{name} is in pageable host memory: allocate it pinned")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        return t.data_ptr()
+    return _dev(t, name)
+
+
+def swap_blocks(src: torch.Tensor, dst: torch.Tensor, block_mapping: torch.Tensor) -> None:
+    """Copy blocks between two pools of the same block shape and dtype (one of
+    them may be a pinned host tensor): dst[block_mapping[i, 1]] :=
+    src[block_mapping[i, 0]].  ``block_mapping`` is int64 [n, 2] on the GPU; the
+    copy runs on the current stream of the GPU pool."""
+    if src.dim() < 2 or tuple(src.shape[1:]) != tuple(dst.shape[1:]) or src.dtype != dst.dtype:
+        raise ValueError("src and dst must be pools [num_blocks, ...] of one block shape and dtype")
+    block_bytes = src[0].numel() * src.element_size()
+    gpu = src if src.device.type == "cuda" else dst
+    if gpu.device.type != "cuda":
+        raise ValueError("one of src and dst must be on the GPU")
+    mp = _mapping(block_mapping)
+    st = library().pa_swap_blocks(_pool(src, "src"), _pool(dst, "dst"), mp,
+                                  int(block_mapping.shape[0]), int(block_bytes), int(src.shape[0]),
+                                  int(dst.shape[0]), _stream(gpu))
+    _check("pa_swap_blocks", st)
 
 
 def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,

@@ -1,0 +1,70 @@
+// Whole-block copies for the block pool (gfx950).
+//
+// Two pool operations the serving engines on the pages build on the block
+// cache:
+// * copy-on-write of a shared block: prefix sharing makes several block
+//   tables name one physical block (wLLM case study, ADR-001 on the KV-cache
+//   layout), so a sequence that is about to write into a shared block first
+//   gets a private copy of it (mini-vLLM README, "Limitations": block
+//   reference counts are kept for prefix caching);
+// * swapping blocks out to host memory and back, which lets a preempted
+//   sequence resume where it stopped (wLLM PyPI page, "Features -- Core
+//   engine": CPU-swap preemption).
+//
+// Both are the same data movement: for each (src, dst) pair of a mapping,
+// copy one block of `block_bytes` from the source pool to the destination
+// pool, for one or two pools (K and V) at once.  A pool may be device memory
+// or host memory the device can address (pinned).  One launch covers every
+// pair: workgroup w copies one 16 KiB chunk of one pair's block, each lane four
+// 16-byte pieces issued before any store, so a chunk keeps 16 KiB of loads in
+// flight per workgroup.
+#include "device_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerLane = 4;                              // 16-byte pieces per lane
+constexpr int64_t kChunk = kThreads * kPerLane * 16;    // bytes per workgroup
+
+__global__ __launch_bounds__(kThreads) void block_copy_kernel(BlockCopyArgs a, int64_t chunks,
+                                                              int64_t total) {
+  for (int64_t w = blockIdx.x; w < total; w += gridDim.x) {
+    const int64_t chunk = w % chunks;
+    const int64_t r = w / chunks;
+    const int64_t pair = r % a.num_pairs;
+    const int pool = static_cast<int>(r / a.num_pairs);
+    const int64_t src_blk = a.block_mapping[2 * pair];
+    const int64_t dst_blk = a.block_mapping[2 * pair + 1];
+    if (src_blk < 0 || src_blk >= a.src_blocks || dst_blk < 0 || dst_blk >= a.dst_blocks) continue;
+    const char* src = static_cast<const char*>(a.src[pool]) + src_blk * a.block_bytes;
+    char* dst = static_cast<char*>(a.dst[pool]) + dst_blk * a.block_bytes;
+    const int64_t base = chunk * kChunk + threadIdx.x * 16;
+    u32x4 v[kPerLane];
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int64_t off = base + i * (kThreads * 16);
+      if (off < a.block_bytes) v[i] = *reinterpret_cast<const u32x4*>(src + off);
+    }
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int64_t off = base + i * (kThreads * 16);
+      if (off < a.block_bytes) *reinterpret_cast<u32x4*>(dst + off) = v[i];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_copy(const BlockCopyArgs& a, hipStream_t stream) {
+  if (a.num_pairs <= 0 || a.num_pools <= 0 || a.block_bytes <= 0) return hipSuccess;
+  const int64_t chunks = (a.block_bytes + kChunk - 1) / kChunk;
+  const int64_t total = chunks * a.num_pairs * a.num_pools;
+  const int64_t grid = total < (int64_t(1) << 20) ? total : (int64_t(1) << 20);  // grid-stride beyond
+  hipLaunchKernelGGL(block_copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                     a, chunks, total);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -122,6 +122,19 @@ pa_status decode_args(void* out, const void* query, const void* key_cache, const
 
 pa_status to_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+// True if a kernel may dereference `p`: device memory, or pinned host memory
+// that HIP maps at the same address.  Pageable host memory (and anything HIP
+// does not know) is refused, since a kernel touching it would fault.
+bool device_addressable(const void* p) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of the failed query
+    return false;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) return true;
+  return attr.type == hipMemoryTypeHost && attr.devicePointer == p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,7 +151,7 @@ const char* pa_status_str(int status) {
   }
 }
 
-int pa_version(void) { return 100; }
+int pa_version(void) { return 101; }
 
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                void* value_cache, const int64_t* slot_mapping,
@@ -156,6 +169,55 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
   pa::CacheWriteArgs a{key, value, key_cache, value_cache, slot_mapping, num_tokens,
                        num_kv_heads, head_dim, log2i(block_size), num_blocks, elem_bytes(dtype)};
   return to_status(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, pa_dtype dtype, void* stream) {
+  if (num_pairs < 0 || num_kv_heads <= 0 || num_blocks < 0) return PA_ERR_BAD_SHAPE;
+  if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!key_cache || !value_cache || !block_mapping) return PA_ERR_NULL_POINTER;
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(block_mapping, 8))
+    return PA_ERR_UNSUPPORTED;
+  pa::BlockCopyArgs a{};
+  a.src[0] = key_cache;
+  a.src[1] = value_cache;
+  a.dst[0] = key_cache;
+  a.dst[1] = value_cache;
+  a.num_pools = 2;
+  a.block_mapping = block_mapping;
+  a.num_pairs = num_pairs;
+  a.block_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
+  a.src_blocks = num_blocks;
+  a.dst_blocks = num_blocks;
+  return to_status(pa::launch_block_copy(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_swap_blocks(const void* src_cache, void* dst_cache, const int64_t* block_mapping,
+                         int32_t num_pairs, int64_t block_bytes, int32_t src_num_blocks,
+                         int32_t dst_num_blocks, void* stream) {
+  if (num_pairs < 0 || block_bytes <= 0 || src_num_blocks < 0 || dst_num_blocks < 0)
+    return PA_ERR_BAD_SHAPE;
+  if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_cache || !dst_cache || !block_mapping) return PA_ERR_NULL_POINTER;
+  if (!aligned(src_cache, 16) || !aligned(dst_cache, 16) || !aligned(block_mapping, 8))
+    return PA_ERR_UNSUPPORTED;
+  if (!device_addressable(src_cache) || !device_addressable(dst_cache) ||
+      !device_addressable(block_mapping))
+    return PA_ERR_UNSUPPORTED;
+  pa::BlockCopyArgs a{};
+  a.src[0] = src_cache;
+  a.dst[0] = dst_cache;
+  a.num_pools = 1;
+  a.block_mapping = block_mapping;
+  a.num_pairs = num_pairs;
+  a.block_bytes = block_bytes;
+  a.src_blocks = src_num_blocks;
+  a.dst_blocks = dst_num_blocks;
+  return to_status(pa::launch_block_copy(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,

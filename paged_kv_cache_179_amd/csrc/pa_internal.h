@@ -28,6 +28,18 @@ struct CacheWriteArgs {
   int32_t elem_bytes;
 };
 
+// Whole-block copies from one or two source pools to destination pools of the
+// same block size (block_ops.hip).
+struct BlockCopyArgs {
+  const void* src[2];
+  void* dst[2];
+  int32_t num_pools;             // 1 or 2 (K and V)
+  const int64_t* block_mapping;  // [num_pairs][2] = (source block, destination block)
+  int64_t num_pairs;
+  int64_t block_bytes;           // multiple of 16
+  int64_t src_blocks, dst_blocks;
+};
+
 struct DecodeArgs {
   void* out;
   const void* query;
@@ -86,6 +98,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);
+hipError_t launch_block_copy(const BlockCopyArgs& a, hipStream_t stream);
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
 // 16-bit caches: the MFMA kernel (decode_mfma.hip), any group size.
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);

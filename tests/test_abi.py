@@ -77,6 +77,39 @@ def test_write_validation(lib):
     assert write(lib, n=0, key=N, value=N, kc=N, vc=N, slots=N) == OK  # empty is a no-op
 
 
+def copy_blocks(lib, kc=P, vc=P, m=P, n=4, hkv=2, d=64, bs=16, nb=8, dt=BF16):
+    return lib.pa_copy_blocks(kc, vc, m, n, hkv, d, bs, nb, dt, N)
+
+
+def swap_blocks(lib, src=P, dst=P, m=P, n=4, bb=4096, sn=8, dn=8):
+    return lib.pa_swap_blocks(src, dst, m, n, bb, sn, dn, N)
+
+
+def test_block_ops_validation(lib):
+    assert copy_blocks(lib, n=-1) == SHAPE
+    assert copy_blocks(lib, hkv=0) == SHAPE
+    assert copy_blocks(lib, nb=-1) == SHAPE
+    assert copy_blocks(lib, d=96) == UNSUP
+    assert copy_blocks(lib, bs=3) == UNSUP
+    assert copy_blocks(lib, dt=7) == UNSUP
+    assert copy_blocks(lib, kc=N) == NULLP
+    assert copy_blocks(lib, vc=N) == NULLP
+    assert copy_blocks(lib, m=N) == NULLP
+    assert copy_blocks(lib, kc=ctypes.c_void_p((1 << 20) + 8)) == UNSUP
+    assert copy_blocks(lib, m=ctypes.c_void_p((1 << 20) + 4)) == UNSUP
+    assert copy_blocks(lib, n=0, kc=N, vc=N, m=N) == OK  # empty is a no-op
+    assert swap_blocks(lib, n=-1) == SHAPE
+    assert swap_blocks(lib, bb=0) == SHAPE
+    assert swap_blocks(lib, sn=-1) == SHAPE
+    assert swap_blocks(lib, dn=-1) == SHAPE
+    assert swap_blocks(lib, bb=24) == UNSUP  # not a multiple of 16
+    assert swap_blocks(lib, src=N) == NULLP
+    assert swap_blocks(lib, dst=N) == NULLP
+    assert swap_blocks(lib, m=N) == NULLP
+    assert swap_blocks(lib, dst=ctypes.c_void_p((1 << 20) + 8)) == UNSUP
+    assert swap_blocks(lib, n=0, src=N, dst=N, m=N) == OK
+
+
 def decode(lib, fn="pa_decode", out=P, q=P, kc=P, vc=P, bt=P, mbps=100, cl=P, s=4, hq=8, hkv=2,
            d=128, bs=16, nb=64, maxc=1000, scale=0.1, part=512, ws=P, wsb=1 << 30, dt=F16):
     return getattr(lib, fn)(out, q, kc, vc, bt, mbps, cl, s, hq, hkv, d, bs, nb, maxc, scale, part,
