@@ -297,7 +297,7 @@ def partition_kernel_name(w):
     if w.dtype == "fp32":
         g = min(8, w.num_heads // w.num_kv_heads)
         return f"decode_partition_kernel<F32,{w.head_dim},{g}>"
-    return f"decode_mfma_kernel<{w.dtype.upper().replace('FP', 'F')},{w.head_dim}>"
+    return f"decode_mfma_kernel<{w.dtype.upper().replace('FP', 'F')},{w.head_dim},ScoreMap<false,false>>"
 
 
 def kernel_source_hash():
@@ -399,6 +399,60 @@ def block_ops(dev, reps=10):
                                          "gbs_one_way": swap_bytes / (ms_in * 1e-3) / 1e9}}
 
 
+def variants(dev, cap=50.0, window=1024, reps=10):
+    """The Gemma-2B-like mixed step with Gemma-2-style logit soft-capping (50)
+    and a 1024-token sliding window, decode and prefill timed apart.  Bytes
+    and flops count only what the window lets each row attend."""
+    from paged_kv_cache_179_amd import workloads as W
+
+    w = W.make("gemma_2b_mixed")
+    st = Step(w, dev)
+    st.write()
+    eb = w.elem_bytes
+    row_kv = w.num_kv_heads * w.head_dim * eb * 2
+    qrow = w.num_heads * w.head_dim * eb
+    ctx = w.context_lens.astype(np.int64)
+    dec_tokens = int(np.minimum(ctx[w.decode_rows], window).sum())
+    dec_bytes = dec_tokens * row_kv + 2 * len(w.decode_rows) * qrow
+    pairs = 0
+    for i, r in enumerate(w.prefill_rows):
+        L = int(w.query_start_loc[i + 1] - w.query_start_loc[i])
+        pos = int(ctx[r]) - L + np.arange(L)
+        pairs += int(np.minimum(pos + 1, window).sum())
+    flops = pairs * w.num_heads * 4 * w.head_dim
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def dec():
+        st.pa.decode(st.out_d, st.q_d, st.kc, st.vc, st.bt_d, st.cl_d, w.scale, st.maxc_d,
+                     partition_size=w.partition_size, workspace=st.ws_d, logit_softcap=cap,
+                     sliding_window=window)
+
+    def pre():
+        st.pa.prefill_chunk(st.out_p, st.q_p, st.qsl, st.kc, st.vc, st.bt_p, st.cl_p, w.scale,
+                            st.maxq, st.maxc_p, workspace=st.ws_p, logit_softcap=cap,
+                            sliding_window=window)
+
+    def timed(fn):
+        ts = []
+        for i in range(reps + 2):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1))
+        return float(np.mean(ts))
+
+    ms_d, ms_p = timed(dec), timed(pre)
+    return {"workload": "gemma_2b_mixed", "logit_softcap": cap, "sliding_window": window,
+            "decode_ms": round(ms_d, 5), "decode_gbs": dec_bytes / (ms_d * 1e-3) / 1e9,
+            "decode_hbm_frac": dec_bytes / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "prefill_ms": round(ms_p, 5), "prefill_tflops": flops / (ms_p * 1e-3) / 1e12,
+            "prefill_mfma_frac": flops / (ms_p * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,10 +514,12 @@ def main():
         del st
         torch.cuda.empty_cache()
 
-    extras = {}
+    extras, variant = {}, None
     if not args.only:
         extras = block_ops(dev)
         log("block ops: " + json.dumps(extras))
+        variant = variants(dev)
+        log("variants: " + json.dumps(variant))
     w, wk, t, r = headline
     part_ms = float(np.mean(t["partitions"]))
     achieved = wk["partition_kernel_bytes"] / (part_ms * 1e-3) / 1e9
@@ -496,6 +552,7 @@ def main():
         "cpu_baseline": results.get("_cpu"),
         "workloads": {k: v for k, v in results.items() if not k.startswith("_")},
         "block_ops": extras or None,
+        "variants": variant,
     }
     print(json.dumps(line), flush=True)
 

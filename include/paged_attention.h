@@ -152,6 +152,15 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
  *   context_lens    int32 [num_seqs]; 0 gives an all-zero output row
  *   max_context_len host-side upper bound of context_lens; sizes the grid
  *   scale           multiplies q.k before the softmax (e.g. 1/sqrt(head_dim))
+ *   logit_softcap   0, or a cap c > 0: every scaled score x becomes
+ *                   c * tanh(x / c) before the softmax
+ *   sliding_window  0, or a window W > 0: a row at position p attends only
+ *                   keys p - W + 1 .. p (its W most recent tokens).  The two
+ *                   are the Gemma-2-style variants that the wLLM PyPI page
+ *                   ("Supported models") names as kernel work; the pages do
+ *                   not define them further, so these are the usual forms.
+ *                   A negative window, or a negative or non-finite cap, is
+ *                   PA_ERR_BAD_SHAPE.
  *   partition_size  tokens per context partition; 0 = never split.  Otherwise
  *                   a positive multiple of 64 and of block_size.  Sequences
  *                   longer than one partition are processed by several
@@ -166,8 +175,9 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t block_size, int32_t num_blocks, int32_t max_context_len,
-                    float scale, int32_t partition_size, void* workspace,
-                    size_t workspace_bytes, pa_dtype dtype, void* stream);
+                    float scale, float logit_softcap, int32_t sliding_window,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    pa_dtype dtype, void* stream);
 
 /*
  * The two halves of pa_decode, for callers that time or schedule them apart
@@ -182,15 +192,16 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
                                int32_t max_blocks_per_seq, const int32_t* context_lens,
                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                               int32_t max_context_len, float scale, int32_t partition_size,
-                               void* workspace, size_t workspace_bytes, pa_dtype dtype,
-                               void* stream);
+                               int32_t max_context_len, float scale, float logit_softcap,
+                               int32_t sliding_window, int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, pa_dtype dtype, void* stream);
 
 pa_status pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
                            int32_t num_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                            int32_t block_size, int32_t max_context_len,
-                           int32_t partition_size, const void* workspace,
-                           size_t workspace_bytes, pa_dtype dtype, void* stream);
+                           int32_t sliding_window, int32_t partition_size,
+                           const void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                           void* stream);
 
 /*
  * Workspace bytes pa_prefill_chunk needs for these sizes (0 if none).
@@ -205,6 +216,8 @@ size_t pa_prefill_workspace_bytes(int32_t num_q_tokens, int32_t num_seqs, int32_
  * context of context_lens[s] tokens that already includes those L tokens (their
  * K/V must be written first).  Row i sits at position C - L + i and attends
  * keys 0 .. C - L + i: the causal mask is aligned to the end of the context.
+ * logit_softcap and sliding_window as for pa_decode (with a window W, row i
+ * attends keys C - L + i - W + 1 .. C - L + i).
  *   out, query       [num_q_tokens][num_heads][head_dim]
  *   query_start_loc  int32 [num_seqs + 1], non-decreasing, last = num_q_tokens
  *   max_query_len    host-side upper bound of the chunk lengths (grid size)
@@ -217,8 +230,9 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                           int32_t max_context_len, float scale, void* workspace,
-                           size_t workspace_bytes, pa_dtype dtype, void* stream);
+                           int32_t max_context_len, float scale, float logit_softcap,
+                           int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                           pa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -3,11 +3,13 @@
 from .attention import (  # noqa: F401
     attend,
     block_of,
+    cap_scores,
     gather,
     kv_head_of,
     paged_decode,
     paged_prefill_chunk,
     query_position,
     reshape_and_cache,
+    window_first_key,
 )
 from .blocks import copy_blocks, swap_blocks  # noqa: F401,E402

@@ -28,6 +28,13 @@ What it computes, and where the pages define it:
   C tokens has its row ``i`` at absolute position ``C - L + i``; it attends to
   keys ``0 .. C - L + i`` (causal, aligned to the end of the context).  A
   decode row is the case L = 1.
+* Two attention variants -- wLLM PyPI page, "Supported models": Gemma 2/3
+  need sliding-window attention and attention-logit soft-capping, which it
+  names as kernel work without defining them.  Read here in their usual
+  (Gemma-2) form: soft-capping at ``c`` replaces each scaled score ``x`` by
+  ``c * tanh(x / c)`` before the softmax; a sliding window of ``W`` tokens lets
+  the row at position ``p`` attend keys ``p - W + 1 .. p`` only.  ``c = 0`` and
+  ``W = 0`` switch them off.
 
 Readings where the pages are silent: cache layout ``[num_blocks, Hkv,
 block_size, D]``; ``context_lens`` counts the current token(s); an empty
@@ -89,8 +96,22 @@ def gather(cache, table_row, context_len: int, block_size: int) -> np.ndarray:
     return out
 
 
-def attend(q, K, V, scale: float, positions, return_weights: bool = False):
-    """softmax(scale * q K^T) V with a causal limit per row.
+def window_first_key(position: int, window: int) -> int:
+    """First key a row at ``position`` attends: the oldest of its ``window``
+    most recent positions (its own included), or 0 without a window."""
+    return max(0, position - window + 1) if window > 0 else 0
+
+
+def cap_scores(z, softcap: float):
+    """Logit soft-capping of scaled scores: ``softcap * tanh(z / softcap)``;
+    ``softcap = 0`` leaves them unchanged."""
+    return softcap * np.tanh(np.asarray(z) / softcap) if softcap > 0 else z
+
+
+def attend(q, K, V, scale: float, positions, return_weights: bool = False,
+           softcap: float = 0.0, window: int = 0):
+    """softmax(cap(scale * q K^T)) V with a causal limit (and optionally a
+    sliding window) per row.
 
     ``q``: [L, Hq, D]; ``K``/``V``: [C, Hkv, D] (contiguous, position order);
     ``positions[i]``: the last key position row ``i`` may attend.  Returns
@@ -104,26 +125,28 @@ def attend(q, K, V, scale: float, positions, return_weights: bool = False):
     out = np.zeros((L, Hq, V.shape[2]), dtype=np.float64)
     weights = np.zeros((L, Hq, C), dtype=np.float64)
     for i in range(L):
-        n = int(positions[i]) + 1  # keys 0 .. positions[i]
+        n = int(positions[i]) + 1  # keys lo .. positions[i]
         if n <= 0:
             continue
+        lo = window_first_key(int(positions[i]), window)
         for h in range(Hq):
             g = kv_head_of(h, Hq, Hkv)
-            z = scale * (K[:n, g, :] @ q[i, h, :])
+            z = cap_scores(scale * (K[lo:n, g, :] @ q[i, h, :]), softcap)
             e = np.exp(z - z.max())
             w = e / e.sum()
-            out[i, h] = w @ V[:n, g, :]
-            weights[i, h, :n] = w
+            out[i, h] = w @ V[lo:n, g, :]
+            weights[i, h, lo:n] = w
     if return_weights:
         return out, weights
     return out
 
 
 def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scale,
-                 block_size, num_kv_heads=None):
+                 block_size, num_kv_heads=None, softcap: float = 0.0, window: int = 0):
     """One decode token per sequence: row ``s`` of ``query`` ([S, Hq, D]) sits
     at position ``context_lens[s] - 1`` and attends all ``context_lens[s]``
-    tokens.  Returns [S, Hq, D] float64 (zeros for an empty context)."""
+    tokens (the last ``window`` of them with a window).  Returns [S, Hq, D]
+    float64 (zeros for an empty context)."""
     query = np.asarray(query, dtype=np.float64)
     S, Hq, D = query.shape
     out = np.zeros((S, Hq, D), dtype=np.float64)
@@ -133,12 +156,13 @@ def paged_decode(query, key_cache, value_cache, block_tables, context_lens, scal
             continue
         K = gather(key_cache, block_tables[s], C, block_size)
         V = gather(value_cache, block_tables[s], C, block_size)
-        out[s] = attend(query[s:s + 1], K, V, scale, [query_position(C, 1, 0)])[0]
+        out[s] = attend(query[s:s + 1], K, V, scale, [query_position(C, 1, 0)],
+                        softcap=softcap, window=window)[0]
     return out
 
 
 def paged_prefill_chunk(query, query_start_loc, key_cache, value_cache, block_tables,
-                        context_lens, scale, block_size):
+                        context_lens, scale, block_size, softcap: float = 0.0, window: int = 0):
     """Chunked-prefill attention.  Sequence ``s`` owns query rows
     ``query_start_loc[s] .. query_start_loc[s+1]-1`` (L rows) and a context of
     ``context_lens[s]`` tokens that already includes the chunk; row ``i`` sits
@@ -154,5 +178,5 @@ def paged_prefill_chunk(query, query_start_loc, key_cache, value_cache, block_ta
         K = gather(key_cache, block_tables[s], C, block_size)
         V = gather(value_cache, block_tables[s], C, block_size)
         pos = [query_position(C, L, i) for i in range(L)]
-        out[a:b] = attend(query[a:b], K, V, scale, pos)
+        out[a:b] = attend(query[a:b], K, V, scale, pos, softcap=softcap, window=window)
     return out

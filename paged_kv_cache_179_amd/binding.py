@@ -36,16 +36,16 @@ _SIGNATURES = {
                        ctypes.c_int),
     "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32], _size),
     "pa_decode": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32, _i32, _i32,
-                   _i32, _i32, _i32, _f32, _i32, _c_ptr, _size, ctypes.c_int, _c_ptr],
+                   _i32, _i32, _i32, _f32, _f32, _i32, _i32, _c_ptr, _size, ctypes.c_int, _c_ptr],
                   ctypes.c_int),
     "pa_decode_partitions": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32,
-                              _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_ptr, _size,
+                              _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _i32, _c_ptr, _size,
                               ctypes.c_int, _c_ptr], ctypes.c_int),
-    "pa_decode_reduce": ([_c_ptr, _c_ptr, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _c_ptr, _size,
-                          ctypes.c_int, _c_ptr], ctypes.c_int),
+    "pa_decode_reduce": ([_c_ptr, _c_ptr, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _c_ptr,
+                          _size, ctypes.c_int, _c_ptr], ctypes.c_int),
     "pa_prefill_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _size),
     "pa_prefill_chunk": ([_c_ptr, _c_ptr, _c_ptr, _i32, _i32, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr,
-                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _c_ptr, _size,
+                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _c_ptr, _size,
                           ctypes.c_int, _c_ptr], ctypes.c_int),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -213,8 +213,11 @@ def _workspace(nbytes: int, like: torch.Tensor, workspace: Optional[torch.Tensor
 def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
            value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
            scale: float, max_context_len: int, partition_size: int = 512,
-           workspace: Optional[torch.Tensor] = None, _fn: str = "pa_decode") -> None:
-    """Paged decode attention into ``out`` ([S, Hq, D]); see pa_decode."""
+           workspace: Optional[torch.Tensor] = None, logit_softcap: float = 0.0,
+           sliding_window: int = 0, _fn: str = "pa_decode") -> None:
+    """Paged decode attention into ``out`` ([S, Hq, D]); see pa_decode.
+    ``logit_softcap`` (0 = none) caps each scaled score x to c * tanh(x / c);
+    ``sliding_window`` (0 = none) limits a row to its W most recent tokens."""
     ptrs, (nb, hkv, bs, d, s, hq, mbps, dt) = _decode_common(out, query, key_cache, value_cache,
                                                              block_tables, context_lens)
     need = decode_workspace_bytes(s, hq, d, max_context_len, partition_size)
@@ -222,8 +225,8 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     fn = getattr(library(), _fn)
     st = fn(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], mbps, ptrs[5], s, hq, hkv, d, bs, nb,
-            int(max_context_len), float(scale), int(partition_size), ws_ptr, nbytes,
-            PA_DTYPE[dt], _stream(out))
+            int(max_context_len), float(scale), float(logit_softcap), int(sliding_window),
+            int(partition_size), ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
     _check(_fn, st)
     return ws
 
@@ -235,8 +238,10 @@ def decode_partitions(*args, **kwargs):
 
 def decode_reduce(out: torch.Tensor, context_lens: torch.Tensor, num_heads: int, head_dim: int,
                   max_blocks_per_seq: int, block_size: int, max_context_len: int,
-                  partition_size: int, workspace: Optional[torch.Tensor]) -> None:
-    """Second half of pa_decode: merge the partition states in ``workspace``."""
+                  partition_size: int, workspace: Optional[torch.Tensor],
+                  sliding_window: int = 0) -> None:
+    """Second half of pa_decode: merge the partition states in ``workspace``
+    (``sliding_window`` as given to decode_partitions)."""
     s = int(context_lens.shape[0])
     dt = out.dtype
     ws_ptr = None if workspace is None else _dev(workspace, "workspace")
@@ -244,8 +249,8 @@ def decode_reduce(out: torch.Tensor, context_lens: torch.Tensor, num_heads: int,
     st = library().pa_decode_reduce(_dev(out, "out", dt), _dev(context_lens, "context_lens",
                                                                torch.int32),
                                     s, num_heads, head_dim, max_blocks_per_seq, block_size,
-                                    int(max_context_len), int(partition_size), ws_ptr, nbytes,
-                                    PA_DTYPE[dt], _stream(out))
+                                    int(max_context_len), int(sliding_window), int(partition_size),
+                                    ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
     _check("pa_decode_reduce", st)
 
 
@@ -259,8 +264,10 @@ def prefill_workspace_bytes(num_q_tokens: int, num_seqs: int, num_heads: int, nu
 def prefill_chunk(out: torch.Tensor, query: torch.Tensor, query_start_loc: torch.Tensor,
                   key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
                   context_lens: torch.Tensor, scale: float, max_query_len: int,
-                  max_context_len: int, workspace: Optional[torch.Tensor] = None) -> None:
-    """Chunked-prefill attention into ``out`` ([num_q_tokens, Hq, D]); see pa_prefill_chunk."""
+                  max_context_len: int, workspace: Optional[torch.Tensor] = None,
+                  logit_softcap: float = 0.0, sliding_window: int = 0) -> None:
+    """Chunked-prefill attention into ``out`` ([num_q_tokens, Hq, D]); see pa_prefill_chunk
+    (``logit_softcap`` and ``sliding_window`` as for decode)."""
     nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
     dt = key_cache.dtype
     if query.dim() != 3 or query.shape[2] != d or out.shape != query.shape:
@@ -280,6 +287,7 @@ def prefill_chunk(out: torch.Tensor, query: torch.Tensor, query_start_loc: torch
         _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
         _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
         _dev(context_lens, "context_lens", torch.int32), s, hq, hkv, d, bs, nb,
-        int(max_context_len), float(scale), ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
+        int(max_context_len), float(scale), float(logit_softcap), int(sliding_window), ws_ptr,
+        nbytes, PA_DTYPE[dt], _stream(out))
     _check("pa_prefill_chunk", st)
     return ws

@@ -47,9 +47,9 @@ struct RowLayout {
   static_assert(kLpt >= 1 && kLpt <= kWave, "row must fit one wave");
 };
 
-template <typename E, int D, int GT>
+template <typename E, int D, int GT, typename S>
 __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
-    DecodeArgs a, int32_t head_chunks, float scale_log2) {
+    DecodeArgs a, int32_t head_chunks, S score) {
   using R = RowLayout<E, D>;
   constexpr int EPL = R::kEpl, LPT = R::kLpt, TPL = R::kTpl, U = R::kUnroll, TILE = R::kTile;
 
@@ -62,7 +62,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   const DecodeItem item = decode_item(a, head_chunks);
   if (!item.valid) return;
   const int seq = item.seq, part = item.part, ctx = item.ctx, kvh = item.kvh, chunk = item.chunk;
-  const int nparts = max(1, (ctx + a.part_tokens - 1) / a.part_tokens);
 
   const int group = a.num_heads / a.num_kv_heads;
   const int h_first = kvh * group + chunk * GT;
@@ -106,8 +105,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   const int64_t lane_bytes = static_cast<int64_t>(sub) * 16;
   const int32_t* table = a.block_tables + static_cast<int64_t>(seq) * a.max_blocks_per_seq;
 
-  const int tok_begin = part * a.part_tokens;
-  const int tok_end = min(tok_begin + a.part_tokens, ctx);
+  const int tok_begin = max(part * a.part_tokens, window_start(a, ctx));
+  const int tok_end = min(part * a.part_tokens + a.part_tokens, ctx);
   for (int seg = tok_begin; seg < tok_end; seg += kSegTokens) {
     const int seg_end = min(seg + kSegTokens, tok_end);
     const int first_blk = seg >> lbs;
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
       for (int h = 0; h < GT; ++h)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const float d = group_sum<LPT>(E::dot(q[h], kr[u], 0.f)) * scale_log2;
+          const float d = score(group_sum<LPT>(E::dot(q[h], kr[u], 0.f)));
           s[h][u] = ok[u] ? d : -__builtin_inff();
         }
 
@@ -217,7 +216,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
       num = __builtin_fmaf(f, s_acc[w][h][d], num);
     }
     const int64_t row = static_cast<int64_t>(seq) * a.num_heads + h_first + h;
-    if (nparts == 1) {
+    if (item.single) {
       E::store(a.out, row * D + d, den == 0.f ? 0.f : num / den);
     } else {
       const int64_t ws = row * a.num_parts + part;
@@ -230,7 +229,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(
   }
 }
 
-template <typename E, int D>
+template <typename E, int D, bool WIN>
 __global__ __launch_bounds__(kDecodeThreads) void decode_reduce_kernel(DecodeArgs a) {
   constexpr int PER = D / kWave;
   const int row = blockIdx.x * kWaves + threadIdx.x / kWave;  // seq * Hq + head
@@ -238,22 +237,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reduce_kernel(DecodeArg
   if (row >= a.num_seqs * a.num_heads) return;
   const int seq = row / a.num_heads;
   const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
-  const int nparts = max(1, (ctx + a.part_tokens - 1) / a.part_tokens);
-  if (nparts <= 1) return;  // written by the partition kernel
+  if (ctx == 0) return;
+  // Partitions holding the attended tokens (the window's, or all of them).
+  const int p0 = WIN ? window_start(a, ctx) / a.part_tokens : 0;
+  const int p1 = (ctx - 1) / a.part_tokens + 1;
+  if (p1 - p0 <= 1) return;  // written by the partition kernel
   const int64_t base = static_cast<int64_t>(row) * a.num_parts;
 
   float mx = -__builtin_inff();
-  for (int p = lane; p < nparts; p += kWave) mx = fmaxf(mx, a.ws_max[base + p]);
+  for (int p = p0 + lane; p < p1; p += kWave) mx = fmaxf(mx, a.ws_max[base + p]);
   mx = across_groups_max<1>(mx);
   const float mu = safe_max(mx);
   float den = 0.f;
-  for (int p = lane; p < nparts; p += kWave) den += exp2_fast(a.ws_max[base + p] - mu) * a.ws_sum[base + p];
+  for (int p = p0 + lane; p < p1; p += kWave) den += exp2_fast(a.ws_max[base + p] - mu) * a.ws_sum[base + p];
   den = across_groups_sum<1>(den);
 
   float num[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) num[j] = 0.f;
-  for (int p = 0; p < nparts; ++p) {
+  for (int p = p0; p < p1; ++p) {
     const float m = a.ws_max[base + p];
     // A partition joined to an earlier one's work item holds no state: its
     // max is -inf, its sum 0, and its partial output was never written.
@@ -275,9 +277,15 @@ hipError_t launch_partitions_gt(const DecodeArgs& a, hipStream_t stream) {
   const uint64_t n = decode_grid(a, chunks);
   if (n == 0) return hipSuccess;
   if (n > 0x7fffffffu) return hipErrorInvalidValue;
-  const float scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((decode_partition_kernel<E, D, GT>), dim3(static_cast<uint32_t>(n)),
-                     dim3(kDecodeThreads), 0, stream, a, chunks, scale_log2);
+  // The window only moves this kernel's token range: no per-score form needed.
+  if (a.softcap > 0.f)
+    hipLaunchKernelGGL((decode_partition_kernel<E, D, GT, ScoreMap<true, false>>),
+                       dim3(static_cast<uint32_t>(n)), dim3(kDecodeThreads), 0, stream, a, chunks,
+                       make_score_map<true, false>(a.scale, a.softcap));
+  else
+    hipLaunchKernelGGL((decode_partition_kernel<E, D, GT, ScoreMap<false, false>>),
+                       dim3(static_cast<uint32_t>(n)), dim3(kDecodeThreads), 0, stream, a, chunks,
+                       make_score_map<false, false>(a.scale, a.softcap));
   return hipGetLastError();
 }
 
@@ -314,13 +322,17 @@ hipError_t launch_partitions_e(const DecodeArgs& a, hipStream_t stream) {
 // ones fill the tail of the partition kernel instead of a long one starting
 // last.  A counting sort over kPlanBuckets length classes (descending); the
 // order inside a class is whatever the LDS atomics give, which changes only
-// the dispatch order, never a result.  One workgroup; it sits on the critical
-// path of every decode call, so it reads each context length once.
+// the dispatch order, never a result.  With a sliding window, a sequence's
+// items start at the partition holding its first attended token, so
+// partitions wholly before the window get no work at all.  One workgroup; it
+// sits on the critical path of every decode call, so it reads each context
+// length once.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = 64;
 constexpr int kSpanTokens = 2048;
 constexpr int kPlanCtxCache = 8192;  // context lengths kept in LDS
 
+template <bool WIN>
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
   __shared__ int hist[3][kPlanBuckets];  // per span choice 1, 2, 4
   __shared__ int s_ctx[kPlanCtxCache];
@@ -341,17 +353,25 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
   auto ctx_of = [&](int s) {
     return s < kPlanCtxCache ? s_ctx[s] : max(0, min(a.context_lens[s], a.ctx_limit));
   };
-  // Tokens of span slot `slot` (of 2^k partitions) of a sequence; a sequence
-  // with an empty context still owns one item, whose output rows are zeros.
-  auto span_tokens = [&](int c, int k, int slot) {
-    return (slot == 0 && c == 0) ? 1 : min(P << k, c - slot * (P << k));
+  // Tokens of span slot `slot` (2^k partitions, counted from the partition
+  // that holds the first attended token `lo`, which starts at token `base`) of
+  // a sequence; a sequence with an empty context still owns one item, whose
+  // output rows are zeros.
+  auto span_tokens = [&](int c, int lo, int base, int k, int slot) {
+    if (slot == 0 && c == 0) return 1;
+    if constexpr (!WIN) return min(P << k, c - slot * (P << k));
+    const int first = base + slot * (P << k);
+    return min(first + (P << k), c) - max(first, lo);
   };
+  auto first_part_token = [&](int lo) { return lo > 0 ? lo - lo % P : 0; };
   for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
     const int c = max(0, min(a.context_lens[s], a.ctx_limit));
     if (s < kPlanCtxCache) s_ctx[s] = c;
+    const int lo = WIN ? window_start(a, c) : 0;
+    const int base = WIN ? first_part_token(lo) : 0;
     for (int k = 0; k <= max_k; ++k)
       for (int slot = 0;; ++slot) {
-        const int t = span_tokens(c, k, slot);
+        const int t = span_tokens(c, lo, base, k, slot);
         if (t <= 0) break;
         atomicAdd(&hist[k][kPlanBuckets - 1 - ((t - 1) >> shift[k])], 1);
       }
@@ -387,27 +407,35 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
   const int span = 1 << k;
   for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
     const int c = ctx_of(s);
-    const int single = c <= P ? 1 : 0;  // one partition: the output is final
+    const int lo = WIN ? window_start(a, c) : 0;
+    const int base = WIN ? first_part_token(lo) : 0;
+    const int p0 = base > 0 ? base / P : 0;
+    const int single = c <= base + P ? 1 : 0;  // one partition: the output is final
     for (int slot = 0;; ++slot) {
-      const int t = span_tokens(c, k, slot);
+      const int t = span_tokens(c, lo, base, k, slot);
       if (t <= 0) break;
       const int pos = atomicAdd(&hist[k][kPlanBuckets - 1 - ((t - 1) >> shift[k])], 1);
-      a.plan[pos] = make_int4(s, slot * span, span | (single << 8), c);
+      a.plan[pos] = make_int4(s, p0 + slot * span, span | (single << 8), c);
     }
   }
 }
 
-template <typename E>
-hipError_t launch_reduce_e(const DecodeArgs& a, hipStream_t stream) {
+template <typename E, bool WIN>
+hipError_t launch_reduce_w(const DecodeArgs& a, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_heads;
   if (rows == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((rows + kWaves - 1) / kWaves));
   switch (a.head_dim) {
-    case 64: hipLaunchKernelGGL((decode_reduce_kernel<E, 64>), grid, dim3(kDecodeThreads), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((decode_reduce_kernel<E, 128>), grid, dim3(kDecodeThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL((decode_reduce_kernel<E, 256>), grid, dim3(kDecodeThreads), 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((decode_reduce_kernel<E, 64, WIN>), grid, dim3(kDecodeThreads), 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((decode_reduce_kernel<E, 128, WIN>), grid, dim3(kDecodeThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((decode_reduce_kernel<E, 256, WIN>), grid, dim3(kDecodeThreads), 0, stream, a); break;
   }
   return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_reduce_e(const DecodeArgs& a, hipStream_t stream) {
+  return a.window > 0 ? launch_reduce_w<E, true>(a, stream) : launch_reduce_w<E, false>(a, stream);
 }
 
 }  // namespace
@@ -443,7 +471,10 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
     const int per = a.num_kv_heads * ((group + 15) / 16);
     a.plan_min_items = std::max(1, (2 * decode_mfma_grid(a) + per - 1) / per);
   }
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  if (a.window > 0)
+    hipLaunchKernelGGL(decode_plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mfma) return launch_decode_mfma(a, stream);

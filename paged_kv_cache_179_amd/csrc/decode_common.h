@@ -15,7 +15,14 @@ namespace pa {
 struct DecodeItem {
   int seq, part, ctx, kvh, chunk;
   bool valid;
+  bool single;  // the sequence's attended tokens lie in one partition: final output
 };
+
+// First token a decode row attends: the start of its sliding window (the
+// window ends at the row's own token, context_lens - 1), or 0 without one.
+__device__ inline int window_start(const DecodeArgs& a, int ctx) {
+  return a.window > 0 ? max(0, ctx - a.window) : 0;
+}
 
 __device__ inline DecodeItem decode_item(const DecodeArgs& a, int head_chunks) {
   const uint32_t per = static_cast<uint32_t>(a.num_kv_heads * head_chunks);
@@ -28,6 +35,7 @@ __device__ inline DecodeItem decode_item(const DecodeArgs& a, int head_chunks) {
   d.seq = it.x;
   d.part = it.y;
   d.ctx = it.w;
+  d.single = (it.z >> 8) & 1;
   d.kvh = static_cast<int>(r) / head_chunks;
   d.chunk = static_cast<int>(r) - d.kvh * head_chunks;
   return d;

@@ -132,15 +132,16 @@ __device__ inline T scalar_ptr(const void* p) {
 struct Unit {
   bool valid;
   int seq, kvh, h_first, nh;
-  int tb, te, ctx;  // token range [tb, te) of the item; context length
+  int tb, te, ctx;  // token range [tb, te) of the item (tb a multiple of 16); context length
+  int lo;           // first attended token (sliding window); tokens below it are masked
   int span;         // partitions joined in the item (its state goes to the first)
   bool single;      // the sequence has one partition: write the output directly
   int mine;         // passes of this wave (passes w, w + 4, ... of the unit)
 };
 
-template <typename E, int D>
+template <typename E, int D, typename S>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs a, int32_t head_chunks,
-                                                                     float scale_log2) {
+                                                                     S score) {
   using M = Mma<E>;
   using G = TileGeo<D>;
   constexpr int NC = G::NC, RB = G::RB, RPI = G::RPI, NDMA = G::NDMA, KB = G::KB, MT = G::MT;
@@ -193,8 +194,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     const int chunk = r - x.kvh * head_chunks;
     x.h_first = x.kvh * group + chunk * kHeadTile;
     x.nh = min(kHeadTile, group - chunk * kHeadTile);
-    x.tb = plan[4 * static_cast<int64_t>(j) + 1] * P;
-    x.te = min(x.tb + x.span * P, x.ctx);
+    const int pb = plan[4 * static_cast<int64_t>(j) + 1] * P;
+    x.lo = window_start(a, x.ctx);
+    // Passes start on a 16-token boundary so that each one stays inside one
+    // block; the tokens before the window in the first pass are masked.
+    x.tb = S::kWindow ? max(pb, x.lo & ~(kTile - 1)) : pb;
+    x.te = min(pb + x.span * P, x.ctx);
     const int npass = (x.valid && x.te > x.tb) ? (x.te - x.tb + kTile - 1) / kTile : 0;
     x.mine = npass > wave ? (npass - wave + kWaves - 1) / kWaves : 0;
     return x;
@@ -289,7 +294,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     // Lane (hl, g4) holds head hl's scores of tokens t0 + 4 g4 + i.
     float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = t0 + 4 * g4 + i < x.te ? s[i] * scale_log2 : -__builtin_inff();
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g4 + i;
+      sc[i] = ((!S::kWindow || t >= x.lo) && t < x.te) ? score(s[i]) : -__builtin_inff();
+    }
     const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     if (__builtin_amdgcn_ballot_w64(mx > m + kLazyMax) != 0) {  // wave-uniform
       const float m_new = fmaxf(m, mx);
@@ -442,7 +450,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
 }
 
 // Workgroups of one persistent launch: as many as fit on the device at once.
-template <typename E, int D>
+template <typename E, int D, typename S>
 int persistent_grid() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -451,7 +459,7 @@ int persistent_grid() {
   if (g > 0) return g;
   int ncu = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D>, kDecodeThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D, S>, kDecodeThreads, 0) !=
       hipSuccess)
     per_cu = 1;
   g = std::max(1, ncu) * std::max(1, per_cu);
@@ -459,13 +467,19 @@ int persistent_grid() {
   return g;
 }
 
-template <typename E>
-int grid_e(int head_dim) {
+template <typename E, typename S>
+int grid_s(int head_dim) {
   switch (head_dim) {
-    case 64: return persistent_grid<E, 64>();
-    case 128: return persistent_grid<E, 128>();
-    default: return persistent_grid<E, 256>();
+    case 64: return persistent_grid<E, 64, S>();
+    case 128: return persistent_grid<E, 128, S>();
+    default: return persistent_grid<E, 256, S>();
   }
+}
+
+template <typename E>
+int grid_e(const DecodeArgs& a) {
+  return with_score_map(a.scale, a.softcap, a.window,
+                        [&](auto map) { return grid_s<E, decltype(map)>(a.head_dim); });
 }
 
 template <typename E, int D>
@@ -474,9 +488,13 @@ hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
   const int chunks = (group + kHeadTile - 1) / kHeadTile;
   const uint64_t n = decode_grid(a, chunks);
   if (n == 0) return hipSuccess;
-  const uint64_t grid = std::min<uint64_t>(n, static_cast<uint64_t>(persistent_grid<E, D>()));
-  hipLaunchKernelGGL((decode_mfma_kernel<E, D>), dim3(static_cast<uint32_t>(grid)), dim3(kDecodeThreads),
-                     0, stream, a, chunks, a.scale * kLog2e);
+  with_score_map(a.scale, a.softcap, a.window, [&](auto map) {
+    using S = decltype(map);
+    const uint64_t grid = std::min<uint64_t>(n, static_cast<uint64_t>(persistent_grid<E, D, S>()));
+    hipLaunchKernelGGL((decode_mfma_kernel<E, D, S>), dim3(static_cast<uint32_t>(grid)),
+                       dim3(kDecodeThreads), 0, stream, a, chunks, map);
+    return 0;
+  });
   return hipGetLastError();
 }
 
@@ -493,7 +511,7 @@ hipError_t launch_e(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 int decode_mfma_grid(const DecodeArgs& a) {
-  return a.dtype == PA_DTYPE_BF16 ? grid_e<BF16>(a.head_dim) : grid_e<F16>(a.head_dim);
+  return a.dtype == PA_DTYPE_BF16 ? grid_e<BF16>(a) : grid_e<F16>(a);
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {

@@ -125,4 +125,40 @@ __device__ inline float safe_max(float m) { return m == -__builtin_inff() ? 0.f 
 
 __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*>(p); }
 
+// Raw score q.k -> exponent of the kernels' base-2 softmax.  Plain attention:
+// scale * s * log2(e).  With logit soft-capping at `cap` (the Gemma-2 style
+// capping that the wLLM PyPI page, "Supported models", names as kernel work):
+// cap * tanh(scale * s / cap) * log2(e), which bounds every score by +-cap.
+// CAP selects the capped form at compile time, so that plain attention
+// carries no tanh in its inner loop; WIN tells the kernels that mask scores
+// one by one whether a sliding window's lower bound takes part (the window
+// itself is in the kernel arguments).
+template <bool CAP, bool WIN>
+struct ScoreMap {
+  static constexpr bool kWindow = WIN;
+  float mul;       // scale * log2(e); scale / cap when capping
+  float cap_log2;  // cap * log2(e) when capping
+  __device__ inline float operator()(float s) const {
+    if constexpr (CAP) return cap_log2 * tanhf(s * mul);
+    return s * mul;
+  }
+};
+template <bool CAP, bool WIN>
+inline ScoreMap<CAP, WIN> make_score_map(float scale, float softcap) {
+  if constexpr (CAP) return ScoreMap<CAP, WIN>{scale / softcap, softcap * kLog2e};
+  return ScoreMap<CAP, WIN>{scale * kLog2e, 0.f};
+}
+
+// Calls launch(map) with the compile-time form of the variant: capped or
+// not, windowed or not.
+template <typename F>
+inline auto with_score_map(float scale, float softcap, int32_t window, F&& launch) {
+  if (softcap > 0.f) {
+    if (window > 0) return launch(make_score_map<true, true>(scale, softcap));
+    return launch(make_score_map<true, false>(scale, softcap));
+  }
+  if (window > 0) return launch(make_score_map<false, true>(scale, softcap));
+  return launch(make_score_map<false, false>(scale, softcap));
+}
+
 }  // namespace pa

@@ -61,6 +61,11 @@ pa_status check_decode_shapes(int32_t num_seqs, int32_t num_heads, int32_t num_k
   return PA_OK;
 }
 
+// Logit soft-cap (>= 0, finite; 0 = none) and sliding window (>= 0; 0 = none).
+bool valid_variant(float logit_softcap, int32_t sliding_window) {
+  return logit_softcap >= 0.f && logit_softcap <= 3.0e38f && sliding_window >= 0;
+}
+
 pa_status check_workspace(size_t needed, const void* workspace, size_t workspace_bytes) {
   if (needed == 0) return PA_OK;
   if (workspace == nullptr) return PA_ERR_NULL_POINTER;
@@ -74,12 +79,15 @@ pa_status decode_args(void* out, const void* query, const void* key_cache, const
                       const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                       int32_t num_blocks, int32_t max_context_len, float scale,
-                      int32_t partition_size, void* workspace, size_t workspace_bytes,
-                      pa_dtype dtype, pa::DecodeArgs* a) {
+                      float logit_softcap, int32_t sliding_window, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                      pa::DecodeArgs* a) {
   pa_status st = check_decode_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                      max_blocks_per_seq, num_blocks, max_context_len,
                                      partition_size, dtype);
-  if (st != PA_OK || num_seqs == 0) return st;
+  if (st != PA_OK) return st;
+  if (!valid_variant(logit_softcap, sliding_window)) return PA_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return st;
   if (!out || !query || !key_cache || !value_cache || !block_tables || !context_lens)
     return PA_ERR_NULL_POINTER;
   if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
@@ -116,6 +124,8 @@ pa_status decode_args(void* out, const void* query, const void* key_cache, const
   a->part_tokens = g.part_tokens;
   a->num_parts = g.num_parts;
   a->scale = scale;
+  a->softcap = logit_softcap;
+  a->window = sliding_window;
   a->dtype = dtype;
   return PA_OK;
 }
@@ -232,24 +242,26 @@ pa_status pa_decode_partitions(void* out, const void* query, const void* key_cac
                                int32_t max_blocks_per_seq, const int32_t* context_lens,
                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                               int32_t max_context_len, float scale, int32_t partition_size,
-                               void* workspace, size_t workspace_bytes, pa_dtype dtype,
-                               void* stream) {
+                               int32_t max_context_len, float scale, float logit_softcap,
+                               int32_t sliding_window, int32_t partition_size, void* workspace,
+                               size_t workspace_bytes, pa_dtype dtype, void* stream) {
   pa::DecodeArgs a;
   pa_status st = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
                              context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
-                             block_size, num_blocks, max_context_len, scale, partition_size,
-                             workspace, workspace_bytes, dtype, &a);
+                             block_size, num_blocks, max_context_len, scale, logit_softcap,
+                             sliding_window, partition_size, workspace, workspace_bytes, dtype,
+                             &a);
   if (st != PA_OK || num_seqs == 0) return st;
   return to_status(pa::launch_decode_partitions(a, static_cast<hipStream_t>(stream)));
 }
 
 pa_status pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
                            int32_t num_heads, int32_t head_dim, int32_t max_blocks_per_seq,
-                           int32_t block_size, int32_t max_context_len, int32_t partition_size,
-                           const void* workspace, size_t workspace_bytes, pa_dtype dtype,
-                           void* stream) {
-  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0) return PA_ERR_BAD_SHAPE;
+                           int32_t block_size, int32_t max_context_len, int32_t sliding_window,
+                           int32_t partition_size, const void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  if (num_seqs < 0 || num_heads <= 0 || max_context_len < 0 || sliding_window < 0)
+    return PA_ERR_BAD_SHAPE;
   if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
     return PA_ERR_UNSUPPORTED;
   if (num_seqs > 0 && max_blocks_per_seq <= 0) return PA_ERR_BAD_SHAPE;
@@ -279,6 +291,7 @@ pa_status pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_s
   a.ctx_limit = g.ctx_limit;
   a.part_tokens = g.part_tokens;
   a.num_parts = g.num_parts;
+  a.window = sliding_window;
   a.dtype = dtype;
   return to_status(pa::launch_decode_reduce(a, static_cast<hipStream_t>(stream)));
 }
@@ -288,13 +301,14 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
                     const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                     int32_t num_blocks, int32_t max_context_len, float scale,
-                    int32_t partition_size, void* workspace, size_t workspace_bytes,
-                    pa_dtype dtype, void* stream) {
+                    float logit_softcap, int32_t sliding_window, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
   pa::DecodeArgs a;
   pa_status st = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
                              context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
-                             block_size, num_blocks, max_context_len, scale, partition_size,
-                             workspace, workspace_bytes, dtype, &a);
+                             block_size, num_blocks, max_context_len, scale, logit_softcap,
+                             sliding_window, partition_size, workspace, workspace_bytes, dtype,
+                             &a);
   if (st != PA_OK || num_seqs == 0) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   st = to_status(pa::launch_decode_partitions(a, s));
@@ -320,9 +334,11 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
                            int32_t max_blocks_per_seq, const int32_t* context_lens,
                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                           int32_t max_context_len, float scale, void* workspace,
-                           size_t workspace_bytes, pa_dtype dtype, void* stream) {
+                           int32_t max_context_len, float scale, float logit_softcap,
+                           int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                           pa_dtype dtype, void* stream) {
   if (num_q_tokens < 0 || max_query_len < 0) return PA_ERR_BAD_SHAPE;
+  if (!valid_variant(logit_softcap, sliding_window)) return PA_ERR_BAD_SHAPE;
   pa_status st = check_decode_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                      max_blocks_per_seq, num_blocks, max_context_len, 0, dtype);
   if (st != PA_OK) return st;
@@ -361,7 +377,9 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
   a.log2_block_size = log2i(block_size);
   a.num_blocks = num_blocks;
   a.ctx_limit = ctx_limit;
+  a.window = sliding_window;
   a.scale = scale;
+  a.softcap = logit_softcap;
   a.dtype = dtype;
   return to_status(pa::launch_prefill(a, workspace, static_cast<hipStream_t>(stream)));
 }

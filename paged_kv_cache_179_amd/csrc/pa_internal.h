@@ -63,7 +63,9 @@ struct DecodeArgs {
   int32_t part_tokens;     // tokens per partition (> 0)
   int32_t num_parts;       // partitions covering ctx_limit
   int32_t plan_min_items;  // the plan may join partitions while it keeps this many items (0: never)
+  int32_t window;          // sliding window (tokens attended, ending at the query); 0 = whole context
   float scale;
+  float softcap;           // logit soft-cap; 0 = none
   pa_dtype dtype;
 };
 
@@ -93,7 +95,9 @@ struct PrefillArgs {
   int32_t log2_block_size;
   int32_t num_blocks;
   int32_t ctx_limit;
+  int32_t window;  // sliding window (keys attended, ending at the row's own position); 0 = none
   float scale;
+  float softcap;   // logit soft-cap; 0 = none
   pa_dtype dtype;
 };
 

@@ -117,9 +117,13 @@ __device__ inline PrefillItem prefill_item(const PrefillArgs& a, int seq, int ti
   if (!it.valid) return it;
   it.npos = min(pos_per_tile, it.qlen - it.pos0);
   it.last_key = it.ctx - it.qlen + it.pos0 + it.npos - 1;  // last key any row of the tile sees
-  it.key_lo = split * kSplitKeys;
-  it.valid = it.key_lo <= it.last_key;
-  it.key_hi = min(it.key_lo + kSplitKeys, it.last_key + 1);
+  // First key any row sees: the window start of the tile's first row.  The
+  // range starts on a pass boundary (keys below the window are masked).
+  const int first_key = a.window > 0 ? max(0, it.ctx - it.qlen + it.pos0 - a.window + 1) : 0;
+  const int split_lo = split * kSplitKeys;
+  it.key_lo = max(split_lo, first_key & ~(kKeyTile - 1));
+  it.valid = split_lo <= it.last_key && split_lo + kSplitKeys > first_key;
+  it.key_hi = min(split_lo + kSplitKeys, it.last_key + 1);
   return it;
 }
 
@@ -173,11 +177,11 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
   }
 }
 
-template <typename E, int D>
+template <typename E, int D, typename S>
 __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs a, int32_t group,
                                                           int32_t pos_per_tile, int32_t nsplit,
                                                           const int4* plan, const int32_t* plan_count,
-                                                          float scale_log2, float* ws_max,
+                                                          S score, float* ws_max,
                                                           float* ws_sum, float* ws_acc) {
   using M = Mma<E>;
   constexpr int NC = D / 8;             // 16-byte chunks per row
@@ -213,9 +217,11 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   const int hl = lane & 15;
   const int g4 = lane >> 4;
 
-  // This lane's two query rows (one per 16-row tile of the wave).
-  int row_lim[NTW], rpos[NTW], rhead[NTW];
+  // This lane's query rows (one per 16-row tile of the wave): the keys
+  // row_lo .. row_lim it attends (row_lo <= 0 without a window).
+  int row_lim[NTW], row_lo[NTW], rpos[NTW], rhead[NTW];
   bool row_ok[NTW];
+  const int win = a.window > 0 ? a.window : 0x40000000;
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     const int row = wave * RPW + 16 * t + hl;
@@ -223,9 +229,11 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
     rhead[t] = row - rpos[t] * group;
     row_ok[t] = rpos[t] < npos;
     row_lim[t] = row_ok[t] ? ctx - qlen + pos0 + rpos[t] : -1;
+    row_lo[t] = row_lim[t] - win + 1;
   }
-  // Last key any row of this wave sees (wave-uniform): passes past it are skipped.
+  // Keys any row of this wave sees (wave-uniform): passes outside are skipped.
   const int wave_last = min(last_key, ctx - qlen + pos0 + min(npos - 1, (wave * RPW + RPW - 1) / group));
+  const int wave_first = ctx - qlen + pos0 + (wave * RPW) / group - win + 1;
 
   // B operands of the scores: lane (hl, g4) of tile t holds dims 32 kb + 8 g4 .. + 7.
   u32x4 q[NTW][KB];
@@ -339,7 +347,8 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int key = k0 + 16 * h + 4 * g4 + i;
-          sc[4 * h + i] = (key <= row_lim[t] && key < key_hi) ? s[h][t][i] * scale_log2 : -__builtin_inff();
+          const bool in = (!S::kWindow || key >= row_lo[t]) && key <= row_lim[t] && key < key_hi;
+          sc[4 * h + i] = in ? score(s[h][t][i]) : -__builtin_inff();
         }
       float mx = sc[0];
 #pragma unroll
@@ -384,14 +393,15 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       default: wait_vmcnt<0>(); break;
     }
     __syncthreads();  // every wave's share of pass p has landed
-    if (key_lo + p * kKeyTile <= wave_last) compute(p, p % NBUF);  // wave-uniform causal skip
+    const int k0 = key_lo + p * kKeyTile;
+    if (k0 <= wave_last && k0 + kKeyTile > wave_first) compute(p, p % NBUF);  // wave-uniform skip
   }
 
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
-    if (!row_ok[t] || key_lo > row_lim[t]) continue;  // no key of this range for this row
+    if (!row_ok[t] || key_lo > row_lim[t] || key_hi <= row_lo[t]) continue;  // no key of this range for this row
     const float lsum = lacc[t][0];
-    const int nsplit_row = (row_lim[t] + kSplitKeys) / kSplitKeys;
+    const int nsplit_row = row_lim[t] / kSplitKeys - max(row_lo[t], 0) / kSplitKeys + 1;
     const int64_t out_row = (static_cast<int64_t>(q_begin) + pos0 + rpos[t]) * a.num_heads + kvh * group + rhead[t];
     // Output register i of tile mt holds dim 16 mt + 4 g4 + i.
     if (nsplit_row == 1) {
@@ -441,21 +451,23 @@ __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(PrefillArgs a, 
   const int pos = t - q_begin;
   if (pos >= qlen) return;
   const int row_lim = ctx - qlen + pos;
-  const int nsplit_row = (row_lim + kSplitKeys) / kSplitKeys;
-  if (nsplit_row <= 1) return;
+  // Key ranges holding the row's keys (those of its window, or 0 .. row_lim).
+  const int p0 = a.window > 0 ? max(0, row_lim - a.window + 1) / kSplitKeys : 0;
+  const int p1 = row_lim / kSplitKeys + 1;
+  if (p1 - p0 <= 1) return;
   const int64_t base = rowid * nsplit;
 
   float mx = -__builtin_inff();
-  for (int p = lane; p < nsplit_row; p += 64) mx = fmaxf(mx, ws_max[base + p]);
+  for (int p = p0 + lane; p < p1; p += 64) mx = fmaxf(mx, ws_max[base + p]);
   mx = across_groups_max<1>(mx);
   const float mu = safe_max(mx);
   float den = 0.f;
-  for (int p = lane; p < nsplit_row; p += 64) den += exp2_fast(ws_max[base + p] - mu) * ws_sum[base + p];
+  for (int p = p0 + lane; p < p1; p += 64) den += exp2_fast(ws_max[base + p] - mu) * ws_sum[base + p];
   den = across_groups_sum<1>(den);
   float num[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) num[j] = 0.f;
-  for (int p = 0; p < nsplit_row; ++p) {
+  for (int p = p0; p < p1; ++p) {
     const float f = exp2_fast(ws_max[base + p] - mu);
 #pragma unroll
     for (int j = 0; j < PER; ++j) num[j] = __builtin_fmaf(f, ws_acc[(base + p) * D + lane * PER + j], num[j]);
@@ -486,8 +498,12 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
                      nsplit, plan, plan_count);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((prefill_kernel<E, D>), dim3(static_cast<uint32_t>(n)), dim3(prefill_threads(D)), 0, stream, a,
-                     group, pos_per_tile, nsplit, plan, plan_count, a.scale * kLog2e, ws_max, ws_sum, ws_acc);
+  with_score_map(a.scale, a.softcap, a.window, [&](auto map) {
+    hipLaunchKernelGGL((prefill_kernel<E, D, decltype(map)>), dim3(static_cast<uint32_t>(n)),
+                       dim3(prefill_threads(D)), 0, stream, a, group, pos_per_tile, nsplit, plan,
+                       plan_count, map, ws_max, ws_sum, ws_acc);
+    return 0;
+  });
   err = hipGetLastError();
   if (err != hipSuccess || nsplit <= 1) return err;
   const int64_t rows = static_cast<int64_t>(a.num_q_tokens) * a.num_heads;

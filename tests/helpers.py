@@ -32,19 +32,20 @@ def written_caches(w):
     return (torch.from_numpy(kc).view(dt), torch.from_numpy(vc).view(dt))
 
 
-def oracle_decode(w, kc, vc, rows=None):
+def oracle_decode(w, kc, vc, rows=None, softcap=0.0, window=0):
     """Oracle decode output for the decode rows (optionally a subset of them)."""
     idx = np.arange(len(w.decode_rows)) if rows is None else np.asarray(rows)
     seqs = w.decode_rows[idx]
     return oracle.paged_decode(f64(w.query_decode)[idx], f64(kc), f64(vc), w.block_tables[seqs],
-                               w.context_lens[seqs], w.scale, w.block_size)
+                               w.context_lens[seqs], w.scale, w.block_size, softcap=softcap,
+                               window=window)
 
 
-def oracle_prefill(w, kc, vc):
+def oracle_prefill(w, kc, vc, softcap=0.0, window=0):
     seqs = w.prefill_rows
     return oracle.paged_prefill_chunk(f64(w.query_prefill), w.query_start_loc, f64(kc), f64(vc),
                                       w.block_tables[seqs], w.context_lens[seqs], w.scale,
-                                      w.block_size)
+                                      w.block_size, softcap=softcap, window=window)
 
 
 def to_dev(w, device):

@@ -111,9 +111,10 @@ def test_block_ops_validation(lib):
 
 
 def decode(lib, fn="pa_decode", out=P, q=P, kc=P, vc=P, bt=P, mbps=100, cl=P, s=4, hq=8, hkv=2,
-           d=128, bs=16, nb=64, maxc=1000, scale=0.1, part=512, ws=P, wsb=1 << 30, dt=F16):
-    return getattr(lib, fn)(out, q, kc, vc, bt, mbps, cl, s, hq, hkv, d, bs, nb, maxc, scale, part,
-                            ws, wsb, dt, N)
+           d=128, bs=16, nb=64, maxc=1000, scale=0.1, cap=0.0, win=0, part=512, ws=P,
+           wsb=1 << 30, dt=F16):
+    return getattr(lib, fn)(out, q, kc, vc, bt, mbps, cl, s, hq, hkv, d, bs, nb, maxc, scale, cap,
+                            win, part, ws, wsb, dt, N)
 
 
 @pytest.mark.parametrize("fn", ["pa_decode", "pa_decode_partitions"])
@@ -127,6 +128,11 @@ def test_decode_validation(lib, fn):
     assert decode(lib, fn, part=100) == SHAPE        # not a multiple of 64
     assert decode(lib, fn, part=64, bs=128) == SHAPE  # not a multiple of block_size
     assert decode(lib, fn, mbps=0) == SHAPE
+    assert decode(lib, fn, cap=-1.0) == SHAPE
+    assert decode(lib, fn, cap=float("nan")) == SHAPE
+    assert decode(lib, fn, cap=float("inf")) == SHAPE
+    assert decode(lib, fn, win=-1) == SHAPE
+    assert decode(lib, fn, cap=30.0, win=64, ws=N) == NULLP  # valid variant, then the workspace check
     assert decode(lib, fn, nb=0) == SHAPE
     assert decode(lib, fn, out=N) == NULLP
     assert decode(lib, fn, cl=N) == NULLP
@@ -141,11 +147,12 @@ def test_decode_validation(lib, fn):
 def test_reduce_validation(lib):
     r = lib.pa_decode_reduce
     # mbps 100 x block 16 >= 1000 tokens: two partitions, so a workspace is needed.
-    assert r(P, P, 4, 8, 128, 100, 16, 1000, 512, N, 0, F16, N) == NULLP
-    assert r(P, P, 4, 8, 128, 100, 16, 1000, 512, P, 10, F16, N) == WS
-    assert r(P, P, 4, 8, 96, 100, 16, 1000, 512, P, 1 << 30, F16, N) == UNSUP
-    assert r(N, P, 4, 8, 128, 100, 16, 1000, 512, P, 1 << 30, F16, N) == NULLP
-    assert r(P, P, 4, 8, 128, 100, 16, 1000, 100, P, 1 << 30, F16, N) == SHAPE
+    assert r(P, P, 4, 8, 128, 100, 16, 1000, 0, 512, N, 0, F16, N) == NULLP
+    assert r(P, P, 4, 8, 128, 100, 16, 1000, 0, 512, P, 10, F16, N) == WS
+    assert r(P, P, 4, 8, 96, 100, 16, 1000, 0, 512, P, 1 << 30, F16, N) == UNSUP
+    assert r(N, P, 4, 8, 128, 100, 16, 1000, 0, 512, P, 1 << 30, F16, N) == NULLP
+    assert r(P, P, 4, 8, 128, 100, 16, 1000, 0, 100, P, 1 << 30, F16, N) == SHAPE
+    assert r(P, P, 4, 8, 128, 100, 16, 1000, -1, 512, P, 1 << 30, F16, N) == SHAPE
 
 
 def test_workspace_sizes(lib):
@@ -170,13 +177,16 @@ def test_workspace_sizes(lib):
 
 
 def prefill(lib, out=P, q=P, qsl=P, nq=64, maxq=32, kc=P, vc=P, bt=P, mbps=8, cl=P, s=2, hq=8,
-            hkv=1, d=256, bs=16, nb=64, maxc=100, scale=0.1, ws=P, wsb=1 << 30, dt=BF16):
+            hkv=1, d=256, bs=16, nb=64, maxc=100, scale=0.1, cap=0.0, win=0, ws=P, wsb=1 << 30,
+            dt=BF16):
     return lib.pa_prefill_chunk(out, q, qsl, nq, maxq, kc, vc, bt, mbps, cl, s, hq, hkv, d, bs, nb,
-                                maxc, scale, ws, wsb, dt, N)
+                                maxc, scale, cap, win, ws, wsb, dt, N)
 
 
 def test_prefill_validation(lib):
     assert prefill(lib, dt=F32) == UNSUP
+    assert prefill(lib, cap=-0.5) == SHAPE
+    assert prefill(lib, win=-3) == SHAPE
     assert prefill(lib, hq=256, hkv=1) == UNSUP     # group larger than a tile
     assert prefill(lib, nq=-1) == SHAPE
     assert prefill(lib, hkv=3) == SHAPE
