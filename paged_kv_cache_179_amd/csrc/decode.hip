@@ -279,9 +279,9 @@ hipError_t launch_partitions_gt(const DecodeArgs& a, hipStream_t stream) {
   if (n > 0x7fffffffu) return hipErrorInvalidValue;
   // The window only moves this kernel's token range: no per-score form needed.
   if (a.softcap > 0.f)
-    hipLaunchKernelGGL((decode_partition_kernel<E, D, GT, ScoreMap<true, false>>),
+    hipLaunchKernelGGL((decode_partition_kernel<E, D, GT, ScoreMap<true, false, true>>),
                        dim3(static_cast<uint32_t>(n)), dim3(kDecodeThreads), 0, stream, a, chunks,
-                       make_score_map<true, false>(a.scale, a.softcap));
+                       make_score_map<true, false, true>(a.scale, a.softcap));
   else
     hipLaunchKernelGGL((decode_partition_kernel<E, D, GT, ScoreMap<false, false>>),
                        dim3(static_cast<uint32_t>(n)), dim3(kDecodeThreads), 0, stream, a, chunks,

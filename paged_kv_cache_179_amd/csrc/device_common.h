@@ -132,21 +132,29 @@ __device__ inline u32x4 load16(const void* p) { return *static_cast<const u32x4*
 // CAP selects the capped form at compile time, so that plain attention
 // carries no tanh in its inner loop; WIN tells the kernels that mask scores
 // one by one whether a sliding window's lower bound takes part (the window
-// itself is in the kernel arguments).
-template <bool CAP, bool WIN>
+// itself is in the kernel arguments).  The capped form evaluates
+// tanh(y) = 1 - 2 / (1 + e^(2y)) with the hardware exp2 and reciprocal (a few
+// instructions; absolute error a few 1e-7, which the cap scales), except in
+// the fp32 kernel (PRECISE), which calls the library tanhf.
+template <bool CAP, bool WIN, bool PRECISE = false>
 struct ScoreMap {
   static constexpr bool kWindow = WIN;
-  float mul;       // scale * log2(e); scale / cap when capping
+  float mul;       // scale * log2(e); without capping the whole map
   float cap_log2;  // cap * log2(e) when capping
+  float cap_in;    // 2 * scale / cap * log2(e): exp2 argument of e^(2y), y = scale * s / cap
   __device__ inline float operator()(float s) const {
-    if constexpr (CAP) return cap_log2 * tanhf(s * mul);
+    if constexpr (CAP) {
+      if constexpr (PRECISE) return cap_log2 * tanhf(s * mul);
+      return cap_log2 * (1.f - 2.f * __builtin_amdgcn_rcpf(1.f + exp2_fast(s * cap_in)));
+    }
     return s * mul;
   }
 };
-template <bool CAP, bool WIN>
-inline ScoreMap<CAP, WIN> make_score_map(float scale, float softcap) {
-  if constexpr (CAP) return ScoreMap<CAP, WIN>{scale / softcap, softcap * kLog2e};
-  return ScoreMap<CAP, WIN>{scale * kLog2e, 0.f};
+template <bool CAP, bool WIN, bool PRECISE = false>
+inline ScoreMap<CAP, WIN, PRECISE> make_score_map(float scale, float softcap) {
+  if constexpr (CAP)
+    return ScoreMap<CAP, WIN, PRECISE>{scale / softcap, softcap * kLog2e, 2.f * scale / softcap * kLog2e};
+  return ScoreMap<CAP, WIN, PRECISE>{scale * kLog2e, 0.f, 0.f};
 }
 
 // Calls launch(map) with the compile-time form of the variant: capped or
