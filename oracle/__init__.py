@@ -13,3 +13,4 @@ from .attention import (  # noqa: F401
     window_first_key,
 )
 from .blocks import copy_blocks, swap_blocks  # noqa: F401,E402
+from .fp8 import dequantize as fp8_dequantize, reshape_and_cache_fp8  # noqa: F401,E402
