@@ -18,7 +18,8 @@
  *                         Core engine": chunked prefill).
  *
  * Two block-pool operations sit beside them: pa_copy_blocks (copy-on-write of
- * a shared block) and pa_swap_blocks (blocks to and from a host pool).
+ * a shared block) and pa_swap_blocks (blocks to and from a host pool); the
+ * _fp8 calls at the end are the same operations over E4M3 caches.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -233,6 +234,69 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
                            int32_t max_context_len, float scale, float logit_softcap,
                            int32_t sliding_window, void* workspace, size_t workspace_bytes,
                            pa_dtype dtype, void* stream);
+
+/*
+ * fp8 KV cache.  The vLLM native-Windows build README lists fp8 among its
+ * KV-cache compression options ("KV compression" column of its release
+ * table); the pages say no more, so this is the usual form: each cached K and
+ * V element is one byte in the OCP 8-bit float format E4M3 (bias 7, 3
+ * mantissa bits, subnormals, no infinities, S.1111.111 = NaN, largest finite
+ * 448) and a cached value is byte * k_scale (K) or byte * v_scale (V), one
+ * scale per tensor.  The caches are uint8 [num_blocks][num_kv_heads]
+ * [block_size][head_dim]; everything else is as in the calls above.
+ *
+ * pa_reshape_and_cache_fp8: the slot-mapped write, quantising each element:
+ * byte = E4M3(key / k_scale) -- the division correctly rounded in fp32, then
+ * round to nearest with ties to even, saturating to +-448; NaN -> 0x7F.  key
+ * and value are `dtype` (F32, F16 or BF16).  k_scale, v_scale > 0 and finite,
+ * else PA_ERR_BAD_SHAPE.
+ */
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                   void* value_cache, const int64_t* slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                                   float k_scale, float v_scale, void* stream);
+
+/*
+ * Decode (and its first half) over E4M3 caches: as pa_decode /
+ * pa_decode_partitions with the K and V scales; the second half is the same
+ * pa_decode_reduce.  `dtype` (query and output) must be F16 or BF16 (else
+ * PA_ERR_UNSUPPORTED).  The bytes are widened exactly to `dtype` in LDS; the K
+ * scale multiplies the scores and the V scale the output.
+ */
+pa_status pa_decode_fp8(void* out, const void* query, const void* key_cache,
+                        const void* value_cache, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                        float scale, float logit_softcap, int32_t sliding_window,
+                        int32_t partition_size, float k_scale, float v_scale, void* workspace,
+                        size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+pa_status pa_decode_partitions_fp8(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_context_len, float scale, float logit_softcap,
+                                   int32_t sliding_window, int32_t partition_size, float k_scale,
+                                   float v_scale, void* workspace, size_t workspace_bytes,
+                                   pa_dtype dtype, void* stream);
+
+/*
+ * Chunked prefill over E4M3 caches: as pa_prefill_chunk with the K and V
+ * scales (same workspace size).
+ */
+pa_status pa_prefill_chunk_fp8(void* out, const void* query, const int32_t* query_start_loc,
+                               int32_t num_q_tokens, int32_t max_query_len, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               int32_t max_context_len, float scale, float logit_softcap,
+                               int32_t sliding_window, float k_scale, float v_scale,
+                               void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                               void* stream);
 
 #ifdef __cplusplus
 }

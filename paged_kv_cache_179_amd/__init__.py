@@ -18,5 +18,6 @@ from .binding import (  # noqa: F401
     prefill_chunk,
     prefill_workspace_bytes,
     reshape_and_cache,
+    reshape_and_cache_fp8,
     swap_blocks,
 )

@@ -19,6 +19,8 @@ _LIB_NAME = "libpaged_attention.so"
 _lib = None
 
 PA_DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+# E4M3 caches (see pa_reshape_and_cache_fp8): bytes, viewed either way.
+FP8_CACHE = (torch.uint8, torch.float8_e4m3fn)
 
 _c_ptr = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -43,6 +45,17 @@ _SIGNATURES = {
                               ctypes.c_int, _c_ptr], ctypes.c_int),
     "pa_decode_reduce": ([_c_ptr, _c_ptr, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _c_ptr,
                           _size, ctypes.c_int, _c_ptr], ctypes.c_int),
+    "pa_reshape_and_cache_fp8": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _i32, _i32, _i32, _i32,
+                                  ctypes.c_int, _f32, _f32, _c_ptr], ctypes.c_int),
+    "pa_decode_fp8": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32, _i32, _i32,
+                       _i32, _i32, _i32, _f32, _f32, _i32, _i32, _f32, _f32, _c_ptr, _size,
+                       ctypes.c_int, _c_ptr], ctypes.c_int),
+    "pa_decode_partitions_fp8": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32,
+                                  _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _i32, _f32, _f32,
+                                  _c_ptr, _size, ctypes.c_int, _c_ptr], ctypes.c_int),
+    "pa_prefill_chunk_fp8": ([_c_ptr, _c_ptr, _c_ptr, _i32, _i32, _c_ptr, _c_ptr, _c_ptr, _i32,
+                              _c_ptr, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32,
+                              _f32, _f32, _c_ptr, _size, ctypes.c_int, _c_ptr], ctypes.c_int),
     "pa_prefill_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _size),
     "pa_prefill_chunk": ([_c_ptr, _c_ptr, _c_ptr, _i32, _i32, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr,
                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _c_ptr, _size,
@@ -102,6 +115,17 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
+def _is_fp8(cache: torch.Tensor) -> bool:
+    return cache.dtype in FP8_CACHE
+
+
+def _scales(key_cache: torch.Tensor, k_scale, v_scale):
+    """(k_scale, v_scale) for an E4M3 cache; both must be given."""
+    if _is_fp8(key_cache) and (k_scale is None or v_scale is None):
+        raise ValueError("an fp8 (E4M3) cache needs k_scale and v_scale")
+    return (1.0 if k_scale is None else float(k_scale)), (1.0 if v_scale is None else float(v_scale))
+
+
 def _cache_dims(key_cache: torch.Tensor, value_cache: torch.Tensor):
     if key_cache.dim() != 4 or key_cache.shape != value_cache.shape:
         raise ValueError("caches must both be [num_blocks, num_kv_heads, block_size, head_dim]")
@@ -126,6 +150,27 @@ def reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.T
         _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
         n, hkv, d, bs, nb, PA_DTYPE[dt], _stream(key_cache))
     _check("pa_reshape_and_cache", st)
+
+
+def reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                          value_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float,
+                          v_scale: float) -> None:
+    """Write key/value [N, Hkv, D] (fp32/fp16/bf16) into E4M3 caches (uint8)
+    at ``slot_mapping``, quantised with the per-tensor scales."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    if not _is_fp8(key_cache):
+        raise TypeError("reshape_and_cache_fp8 writes uint8 (E4M3) caches")
+    dt = key.dtype
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim] matching the cache")
+    n = int(key.shape[0])
+    if tuple(slot_mapping.shape) != (n,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    st = library().pa_reshape_and_cache_fp8(
+        _dev(key, "key", dt), _dev(value, "value", dt), _dev(key_cache, "key_cache"),
+        _dev(value_cache, "value_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
+        n, hkv, d, bs, nb, PA_DTYPE[dt], float(k_scale), float(v_scale), _stream(key_cache))
+    _check("pa_reshape_and_cache_fp8", st)
 
 
 def _mapping(block_mapping: torch.Tensor) -> int:
@@ -186,7 +231,9 @@ def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_con
 
 def _decode_common(out, query, key_cache, value_cache, block_tables, context_lens):
     nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
-    dt = key_cache.dtype
+    dt = query.dtype
+    if not _is_fp8(key_cache) and key_cache.dtype != dt:
+        raise TypeError("query and cache dtypes differ")
     if query.dim() != 3 or query.shape[2] != d or out.shape != query.shape:
         raise ValueError("query/out must be [num_seqs, num_heads, head_dim] matching the cache")
     s, hq = int(query.shape[0]), int(query.shape[1])
@@ -214,20 +261,26 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
            value_cache: torch.Tensor, block_tables: torch.Tensor, context_lens: torch.Tensor,
            scale: float, max_context_len: int, partition_size: int = 512,
            workspace: Optional[torch.Tensor] = None, logit_softcap: float = 0.0,
-           sliding_window: int = 0, _fn: str = "pa_decode") -> None:
+           sliding_window: int = 0, k_scale: Optional[float] = None,
+           v_scale: Optional[float] = None, _fn: str = "pa_decode") -> None:
     """Paged decode attention into ``out`` ([S, Hq, D]); see pa_decode.
     ``logit_softcap`` (0 = none) caps each scaled score x to c * tanh(x / c);
-    ``sliding_window`` (0 = none) limits a row to its W most recent tokens."""
+    ``sliding_window`` (0 = none) limits a row to its W most recent tokens.
+    uint8 (E4M3) caches take ``k_scale`` and ``v_scale`` (pa_decode_fp8)."""
     ptrs, (nb, hkv, bs, d, s, hq, mbps, dt) = _decode_common(out, query, key_cache, value_cache,
                                                              block_tables, context_lens)
     need = decode_workspace_bytes(s, hq, d, max_context_len, partition_size)
     ws, ws_ptr = _workspace(need, out, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    fn = getattr(library(), _fn)
-    st = fn(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], mbps, ptrs[5], s, hq, hkv, d, bs, nb,
+    args = [ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], mbps, ptrs[5], s, hq, hkv, d, bs, nb,
             int(max_context_len), float(scale), float(logit_softcap), int(sliding_window),
-            int(partition_size), ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
-    _check(_fn, st)
+            int(partition_size)]
+    name = _fn
+    if _is_fp8(key_cache):
+        name = _fn + "_fp8"
+        args += list(_scales(key_cache, k_scale, v_scale))
+    st = getattr(library(), name)(*args, ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
+    _check(name, st)
     return ws
 
 
@@ -265,11 +318,15 @@ def prefill_chunk(out: torch.Tensor, query: torch.Tensor, query_start_loc: torch
                   key_cache: torch.Tensor, value_cache: torch.Tensor, block_tables: torch.Tensor,
                   context_lens: torch.Tensor, scale: float, max_query_len: int,
                   max_context_len: int, workspace: Optional[torch.Tensor] = None,
-                  logit_softcap: float = 0.0, sliding_window: int = 0) -> None:
+                  logit_softcap: float = 0.0, sliding_window: int = 0,
+                  k_scale: Optional[float] = None, v_scale: Optional[float] = None) -> None:
     """Chunked-prefill attention into ``out`` ([num_q_tokens, Hq, D]); see pa_prefill_chunk
-    (``logit_softcap`` and ``sliding_window`` as for decode)."""
+    (``logit_softcap``, ``sliding_window``, and the scales of uint8 (E4M3) caches as for
+    decode)."""
     nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
-    dt = key_cache.dtype
+    dt = query.dtype
+    if not _is_fp8(key_cache) and key_cache.dtype != dt:
+        raise TypeError("query and cache dtypes differ")
     if query.dim() != 3 or query.shape[2] != d or out.shape != query.shape:
         raise ValueError("query/out must be [num_q_tokens, num_heads, head_dim]")
     nq, hq = int(query.shape[0]), int(query.shape[1])
@@ -281,13 +338,16 @@ def prefill_chunk(out: torch.Tensor, query: torch.Tensor, query_start_loc: torch
     need = prefill_workspace_bytes(nq, s, hq, hkv, d, max_query_len, max_context_len)
     ws, ws_ptr = _workspace(need, out, workspace)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    st = library().pa_prefill_chunk(
-        _dev(out, "out", dt), _dev(query, "query", dt),
-        _dev(query_start_loc, "query_start_loc", torch.int32), nq, int(max_query_len),
-        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
-        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
-        _dev(context_lens, "context_lens", torch.int32), s, hq, hkv, d, bs, nb,
-        int(max_context_len), float(scale), float(logit_softcap), int(sliding_window), ws_ptr,
-        nbytes, PA_DTYPE[dt], _stream(out))
-    _check("pa_prefill_chunk", st)
+    args = [_dev(out, "out", dt), _dev(query, "query", dt),
+            _dev(query_start_loc, "query_start_loc", torch.int32), nq, int(max_query_len),
+            _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+            _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+            _dev(context_lens, "context_lens", torch.int32), s, hq, hkv, d, bs, nb,
+            int(max_context_len), float(scale), float(logit_softcap), int(sliding_window)]
+    name = "pa_prefill_chunk"
+    if _is_fp8(key_cache):
+        name = "pa_prefill_chunk_fp8"
+        args += list(_scales(key_cache, k_scale, v_scale))
+    st = getattr(library(), name)(*args, ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
+    _check(name, st)
     return ws

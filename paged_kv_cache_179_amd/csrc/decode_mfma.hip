@@ -55,6 +55,7 @@ constexpr int kHeadTile = 16;   // query heads per workgroup (MFMA N)
 constexpr float kLazyMax = 8.f; // log2 of the largest unnormalised probability
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -78,6 +79,14 @@ struct Mma<BF16> {
     const bf16x2 r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
     return __builtin_bit_cast(unsigned, r);
   }
+  // Two E4M3 values (the low or high half of w) as a bf16 pair.  Exact: the
+  // hardware conversion gives the fp32 value, whose 4 significant bits all
+  // sit in the upper half that bf16 keeps.
+  template <bool HIGH>
+  __device__ static inline unsigned from_fp8(unsigned w) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
+    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+  }
 };
 template <>
 struct Mma<F16> {
@@ -93,6 +102,13 @@ struct Mma<F16> {
   __device__ static inline unsigned pack(float lo, float hi) {
     const f16x2 r = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
     return __builtin_bit_cast(unsigned, r);
+  }
+  // Two E4M3 values as an fp16 pair; every E4M3 value is an fp16 value, so
+  // the (truncating) packed conversion is exact.
+  template <bool HIGH>
+  __device__ static inline unsigned from_fp8(unsigned w) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(f[0], f[1]));
   }
 };
 
@@ -139,24 +155,40 @@ struct Unit {
   int mine;         // passes of this wave (passes w, w + 4, ... of the unit)
 };
 
-template <typename E, int D, typename S>
+template <typename E, int D, typename S, bool KV8>
 __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs a, int32_t head_chunks,
                                                                      S score) {
   using M = Mma<E>;
   using G = TileGeo<D>;
-  constexpr int NC = G::NC, RB = G::RB, RPI = G::RPI, NDMA = G::NDMA, KB = G::KB, MT = G::MT;
+  constexpr int NC = G::NC, RB = G::RB, RPI = G::RPI, KB = G::KB, MT = G::MT;
+  // Cached rows: 2 D bytes (16-bit) or D bytes (E4M3, converted in LDS to the
+  // 16-bit tile the MFMAs read).
+  constexpr int CRB = KV8 ? D : RB;            // cached row bytes
+  constexpr int CNC = CRB / 16;                // 16-byte chunks per cached row
+  constexpr int CRPI = 1024 / CRB;             // cached rows per DMA instruction
+  constexpr int NDMA = kTile / CRPI;           // DMA instructions per pass, K or V
   constexpr int NQ = kHeadTile * RB / 1024;  // DMA instructions per query tile
   
   // Per wave, two pipeline slots, each a key tile and a value tile of
   // [kTile rows][NC chunks].  A slot is exactly one wave's partial output
   // [16 heads][D] in fp32, which is where that goes at the end of a unit.
-  __shared__ u32x4 s_kv[kWaves][2][2][kTile][NC];
+  __shared__ u32x4 s_kv[kWaves][2][2][kTile][CNC];
+  // E4M3 caches: each wave's converted K and V tile of the pass it computes,
+  // rotated as the 16-bit slots are; also where its partial output goes.
+  __shared__ u32x4 s_cv[KV8 ? kWaves : 1][2][kTile][KV8 ? NC : 1];
   // Query tile of the current unit and of the next one.
   __shared__ u32x4 s_q[2][kHeadTile][NC];
   __shared__ float s_max[kWaves][kHeadTile];
   __shared__ float s_sum[kWaves][kHeadTile];
   __shared__ int s_part[kWaves];
-  static_assert(sizeof(s_kv[0][0]) == kHeadTile * D * sizeof(float), "partial output fills a slot");
+  static_assert((KV8 ? sizeof(s_cv[0]) : sizeof(s_kv[0][0])) == kHeadTile * D * sizeof(float),
+                "partial output fills a slot");
+  // K and V tile a wave's MFMAs read for the pass in slot `sl`, and the place
+  // of its partial output.
+  auto kv_tile = [&](int w, int sl) -> char* {
+    if constexpr (KV8) return reinterpret_cast<char*>(&s_cv[w][0][0][0]);
+    return reinterpret_cast<char*>(&s_kv[w][sl][0][0][0]);
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -227,6 +259,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     const char* kd = reinterpret_cast<const char*>(&s_kv[wave][sl][0][0][0]);
     const char* vd = reinterpret_cast<const char*>(&s_kv[wave][sl][1][0][0]);
     const int64_t trow = static_cast<int64_t>(x.seq) * a.max_blocks_per_seq;
+    if constexpr (KV8) {
+      // E4M3 rows land unrotated; the conversion applies the rotations.
+#pragma unroll
+      for (int r = 0; r < NDMA; ++r) {
+        const int row = r * CRPI + lane / CNC;
+        const int t = min(t0 + row, x.te - 1);
+        int b;
+        if (lbs >= 4) {
+          b = tables[trow + (t0 >> lbs)];
+        } else {
+          b = a.block_tables[trow + (t >> lbs)];
+        }
+        b = (b < 0 || b >= a.num_blocks) ? 0 : b;
+        const int64_t roff =
+            ((((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) | (t & off_mask)) * CRB) +
+            (lane % CNC) * 16;
+        dma16(kbase + roff, kd + r * 1024);
+        dma16(vbase + roff, vd + r * 1024);
+      }
+      return;
+    }
     if (lbs >= 4) {
       // The 16 tokens lie in one block: one scalar table read per pass.
       int b = tables[trow + (t0 >> lbs)];
@@ -274,6 +327,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     }
   };
 
+  // E4M3 caches: convert this wave's pass in slot `sl` into its 16-bit tile.
+  // Lane l takes 16-byte chunks l, l + 64, ... (chunk q: row q / CNC, dims
+  // 16 (q % CNC) ..+15) and writes the two 16-bit chunks they become at their
+  // rotated places.
+  auto convert = [&](int sl) {
+    if constexpr (KV8) {
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+#pragma unroll
+        for (int i = 0; i < kTile * CNC / 64; ++i) {
+          const int q = lane + 64 * i;
+          const int t = q / CNC;
+          const int c = 2 * (q % CNC);
+          const u32x4 w = s_kv[wave][sl][kv][t][q % CNC];
+          const u32x4 lo = {M::template from_fp8<false>(w[0]), M::template from_fp8<true>(w[0]),
+                            M::template from_fp8<false>(w[1]), M::template from_fp8<true>(w[1])};
+          const u32x4 hi = {M::template from_fp8<false>(w[2]), M::template from_fp8<true>(w[2]),
+                            M::template from_fp8<false>(w[3]), M::template from_fp8<true>(w[3])};
+          const int rot = kv == 0 ? G::rot_k(t) : G::rot_v(t);
+          s_cv[wave][kv][t][(c - rot + NC) % NC] = lo;
+          s_cv[wave][kv][t][(c + 1 - rot + NC) % NC] = hi;
+        }
+      }
+      wave_lds_sync();
+    }
+  };
+
   const u32x2 ones = {M::kOnePair, M::kOnePair};
   f32x4 acc[MT];
   f32x4 lacc;
@@ -281,8 +361,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
 
   auto compute = [&](const Unit& x, int k, int sl, int qb) {
     const int t0 = x.tb + (k * kWaves + wave) * kTile;
-    const char* kt = reinterpret_cast<const char*>(&s_kv[wave][sl][0][0][0]);
-    const char* vt = reinterpret_cast<const char*>(&s_kv[wave][sl][1][0][0]);
+    const char* kt = kv_tile(wave, sl);
+    const char* vt = kt + kTile * RB;
     const char* qt = reinterpret_cast<const char*>(&s_q[qb][0][0]);
 
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
@@ -322,7 +402,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   // Merge of the four waves' partial states of unit x (slot `pr` of each
   // wave holds its partial output) and the output or workspace writes.
   auto finish = [&](const Unit& x, int pr) {
-    float* part_out = reinterpret_cast<float*>(&s_kv[wave][pr][0][0][0]);
+    float* part_out = reinterpret_cast<float*>(kv_tile(wave, pr));
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       *reinterpret_cast<f32x4*>(part_out + hl * D + 16 * mt + 4 * g4) = acc[mt];
@@ -355,8 +435,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
         const float f = exp2_fast(mw[w] - mu);
         den = __builtin_fmaf(f, s_sum[w][h], den);
         num += f * *reinterpret_cast<const f32x4*>(
-                       reinterpret_cast<const float*>(&s_kv[w][s_part[w]][0][0][0]) + h * D + d);
+                       reinterpret_cast<const float*>(kv_tile(w, s_part[w])) + h * D + d);
       }
+      if constexpr (KV8) num *= a.v_scale;  // values were read without their scale
       const int64_t row = static_cast<int64_t>(x.seq) * a.num_heads + x.h_first + h;
       if (x.single) {
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
@@ -426,6 +507,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
         }
       }
       wave_lds_sync();
+      convert(slot);
       compute(cur, k, slot, qb);
       slot ^= 1;
     }
@@ -450,7 +532,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
 }
 
 // Workgroups of one persistent launch: as many as fit on the device at once.
-template <typename E, int D, typename S>
+template <typename E, int D, typename S, bool KV8>
 int persistent_grid() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -459,43 +541,52 @@ int persistent_grid() {
   if (g > 0) return g;
   int ncu = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D, S>, kDecodeThreads, 0) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D, S, KV8>, kDecodeThreads,
+                                                    0) != hipSuccess)
     per_cu = 1;
   g = std::max(1, ncu) * std::max(1, per_cu);
   cache[dev].store(g, std::memory_order_relaxed);
   return g;
 }
 
-template <typename E, typename S>
+template <typename E, typename S, bool KV8>
 int grid_s(int head_dim) {
   switch (head_dim) {
-    case 64: return persistent_grid<E, 64, S>();
-    case 128: return persistent_grid<E, 128, S>();
-    default: return persistent_grid<E, 256, S>();
+    case 64: return persistent_grid<E, 64, S, KV8>();
+    case 128: return persistent_grid<E, 128, S, KV8>();
+    default: return persistent_grid<E, 256, S, KV8>();
   }
 }
 
+// Scale of q.k before the score map: an E4M3 cache's K scale folds in here.
+inline float qk_scale(const DecodeArgs& a) { return a.kv_fp8 ? a.scale * a.k_scale : a.scale; }
+
 template <typename E>
 int grid_e(const DecodeArgs& a) {
-  return with_score_map(a.scale, a.softcap, a.window,
-                        [&](auto map) { return grid_s<E, decltype(map)>(a.head_dim); });
+  return with_score_map(qk_scale(a), a.softcap, a.window, [&](auto map) {
+    return a.kv_fp8 ? grid_s<E, decltype(map), true>(a.head_dim) : grid_s<E, decltype(map), false>(a.head_dim);
+  });
 }
 
-template <typename E, int D>
-hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+template <typename E, int D, bool KV8>
+hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_heads / a.num_kv_heads;
   const int chunks = (group + kHeadTile - 1) / kHeadTile;
   const uint64_t n = decode_grid(a, chunks);
   if (n == 0) return hipSuccess;
-  with_score_map(a.scale, a.softcap, a.window, [&](auto map) {
+  with_score_map(qk_scale(a), a.softcap, a.window, [&](auto map) {
     using S = decltype(map);
-    const uint64_t grid = std::min<uint64_t>(n, static_cast<uint64_t>(persistent_grid<E, D, S>()));
-    hipLaunchKernelGGL((decode_mfma_kernel<E, D, S>), dim3(static_cast<uint32_t>(grid)),
+    const uint64_t grid = std::min<uint64_t>(n, static_cast<uint64_t>(persistent_grid<E, D, S, KV8>()));
+    hipLaunchKernelGGL((decode_mfma_kernel<E, D, S, KV8>), dim3(static_cast<uint32_t>(grid)),
                        dim3(kDecodeThreads), 0, stream, a, chunks, map);
     return 0;
   });
   return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t launch_d(const DecodeArgs& a, hipStream_t stream) {
+  return a.kv_fp8 ? launch_kv<E, D, true>(a, stream) : launch_kv<E, D, false>(a, stream);
 }
 
 template <typename E>

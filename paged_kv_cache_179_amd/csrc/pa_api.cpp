@@ -61,6 +61,9 @@ pa_status check_decode_shapes(int32_t num_seqs, int32_t num_heads, int32_t num_k
   return PA_OK;
 }
 
+// An E4M3 cache scale: positive and finite.
+bool valid_scale(float s) { return s > 0.f && s <= 3.0e38f; }
+
 // Logit soft-cap (>= 0, finite; 0 = none) and sliding window (>= 0; 0 = none).
 bool valid_variant(float logit_softcap, int32_t sliding_window) {
   return logit_softcap >= 0.f && logit_softcap <= 3.0e38f && sliding_window >= 0;
@@ -147,6 +150,70 @@ bool device_addressable(const void* p) {
 
 }  // namespace
 
+namespace {
+
+pa_status prefill_impl(void* out, const void* query, const int32_t* query_start_loc,
+                           int32_t num_q_tokens, int32_t max_query_len, const void* key_cache,
+                           const void* value_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_context_len, float scale, float logit_softcap,
+                           int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                           pa_dtype dtype, int32_t kv_fp8, float k_scale, float v_scale,
+                           void* stream) {
+  if (num_q_tokens < 0 || max_query_len < 0) return PA_ERR_BAD_SHAPE;
+  if (!valid_variant(logit_softcap, sliding_window)) return PA_ERR_BAD_SHAPE;
+  pa_status st = check_decode_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                     max_blocks_per_seq, num_blocks, max_context_len, 0, dtype);
+  if (st != PA_OK) return st;
+  if (dtype == PA_DTYPE_F32 || num_heads / num_kv_heads > 128) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_q_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !query || !query_start_loc || !key_cache || !value_cache || !block_tables ||
+      !context_lens)
+    return PA_ERR_NULL_POINTER;
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(query_start_loc, 4))
+    return PA_ERR_UNSUPPORTED;
+  const int32_t ctx_limit = clamp_i32(
+      std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size));
+  if (ctx_limit == 0) return PA_OK;
+  const pa::PrefillWorkspace w = pa::prefill_workspace_layout(
+      num_q_tokens, num_heads, head_dim, pa::prefill_num_splits(ctx_limit), num_seqs,
+      pa::prefill_num_tiles(num_heads, num_kv_heads, max_query_len));
+  st = check_workspace(w.bytes, workspace, workspace_bytes);
+  if (st != PA_OK) return st;
+  pa::PrefillArgs a{};
+  a.out = out;
+  a.query = query;
+  a.query_start_loc = query_start_loc;
+  a.key_cache = key_cache;
+  a.value_cache = value_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_q_tokens = num_q_tokens;
+  a.max_query_len = max_query_len;
+  a.num_seqs = num_seqs;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.log2_block_size = log2i(block_size);
+  a.num_blocks = num_blocks;
+  a.ctx_limit = ctx_limit;
+  a.window = sliding_window;
+  a.scale = scale;
+  a.softcap = logit_softcap;
+  a.dtype = dtype;
+  a.kv_fp8 = kv_fp8;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return to_status(pa::launch_prefill(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pa_status_str(int status) {
@@ -161,7 +228,7 @@ const char* pa_status_str(int status) {
   }
 }
 
-int pa_version(void) { return 101; }
+int pa_version(void) { return 102; }
 
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                void* value_cache, const int64_t* slot_mapping,
@@ -177,7 +244,28 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cac
       !aligned(value_cache, 16) || !aligned(slot_mapping, 8))
     return PA_ERR_UNSUPPORTED;
   pa::CacheWriteArgs a{key, value, key_cache, value_cache, slot_mapping, num_tokens,
-                       num_kv_heads, head_dim, log2i(block_size), num_blocks, elem_bytes(dtype)};
+                       num_kv_heads, head_dim, log2i(block_size), num_blocks, elem_bytes(dtype),
+                       dtype, 0, 1.f, 1.f};
+  return to_status(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_reshape_and_cache_fp8(const void* key, const void* value, void* key_cache,
+                                   void* value_cache, const int64_t* slot_mapping,
+                                   int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t num_blocks, pa_dtype dtype,
+                                   float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return PA_ERR_BAD_SHAPE;
+  if (!supported_dtype(dtype) || !supported_head_dim(head_dim) || !supported_block_size(block_size))
+    return PA_ERR_UNSUPPORTED;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_BAD_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
+  if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16) || !aligned(slot_mapping, 8))
+    return PA_ERR_UNSUPPORTED;
+  pa::CacheWriteArgs a{key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                       num_kv_heads, head_dim, log2i(block_size), num_blocks, elem_bytes(dtype),
+                       dtype, 1, k_scale, v_scale};
   return to_status(pa::launch_reshape_and_cache(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -316,6 +404,49 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
   return to_status(pa::launch_decode_reduce(a, s));
 }
 
+pa_status pa_decode_partitions_fp8(void* out, const void* query, const void* key_cache,
+                                   const void* value_cache, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                   int32_t max_context_len, float scale, float logit_softcap,
+                                   int32_t sliding_window, int32_t partition_size, float k_scale,
+                                   float v_scale, void* workspace, size_t workspace_bytes,
+                                   pa_dtype dtype, void* stream) {
+  if (dtype != PA_DTYPE_F16 && dtype != PA_DTYPE_BF16) return PA_ERR_UNSUPPORTED;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_BAD_SHAPE;
+  pa::DecodeArgs a;
+  pa_status st = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                             context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, max_context_len, scale, logit_softcap,
+                             sliding_window, partition_size, workspace, workspace_bytes, dtype,
+                             &a);
+  if (st != PA_OK || num_seqs == 0) return st;
+  a.kv_fp8 = 1;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return to_status(pa::launch_decode_partitions(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_decode_fp8(void* out, const void* query, const void* key_cache,
+                        const void* value_cache, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t block_size, int32_t num_blocks, int32_t max_context_len,
+                        float scale, float logit_softcap, int32_t sliding_window,
+                        int32_t partition_size, float k_scale, float v_scale, void* workspace,
+                        size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  pa_status st = pa_decode_partitions_fp8(
+      out, query, key_cache, value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+      num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale,
+      logit_softcap, sliding_window, partition_size, k_scale, v_scale, workspace, workspace_bytes,
+      dtype, stream);
+  if (st != PA_OK || num_seqs == 0) return st;
+  return pa_decode_reduce(out, context_lens, num_seqs, num_heads, head_dim, max_blocks_per_seq,
+                          block_size, max_context_len, sliding_window, partition_size, workspace,
+                          workspace_bytes, dtype, stream);
+}
+
 size_t pa_prefill_workspace_bytes(int32_t num_q_tokens, int32_t num_seqs, int32_t num_heads,
                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_query_len,
                                   int32_t max_context_len) {
@@ -337,51 +468,29 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
                            int32_t max_context_len, float scale, float logit_softcap,
                            int32_t sliding_window, void* workspace, size_t workspace_bytes,
                            pa_dtype dtype, void* stream) {
-  if (num_q_tokens < 0 || max_query_len < 0) return PA_ERR_BAD_SHAPE;
-  if (!valid_variant(logit_softcap, sliding_window)) return PA_ERR_BAD_SHAPE;
-  pa_status st = check_decode_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
-                                     max_blocks_per_seq, num_blocks, max_context_len, 0, dtype);
-  if (st != PA_OK) return st;
-  if (dtype == PA_DTYPE_F32 || num_heads / num_kv_heads > 128) return PA_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || num_q_tokens == 0 || max_query_len == 0) return PA_OK;
-  if (!out || !query || !query_start_loc || !key_cache || !value_cache || !block_tables ||
-      !context_lens)
-    return PA_ERR_NULL_POINTER;
-  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) ||
-      !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      !aligned(query_start_loc, 4))
-    return PA_ERR_UNSUPPORTED;
-  const int32_t ctx_limit = clamp_i32(
-      std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size));
-  if (ctx_limit == 0) return PA_OK;
-  const pa::PrefillWorkspace w = pa::prefill_workspace_layout(
-      num_q_tokens, num_heads, head_dim, pa::prefill_num_splits(ctx_limit), num_seqs,
-      pa::prefill_num_tiles(num_heads, num_kv_heads, max_query_len));
-  st = check_workspace(w.bytes, workspace, workspace_bytes);
-  if (st != PA_OK) return st;
-  pa::PrefillArgs a{};
-  a.out = out;
-  a.query = query;
-  a.query_start_loc = query_start_loc;
-  a.key_cache = key_cache;
-  a.value_cache = value_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.num_q_tokens = num_q_tokens;
-  a.max_query_len = max_query_len;
-  a.num_seqs = num_seqs;
-  a.num_heads = num_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.log2_block_size = log2i(block_size);
-  a.num_blocks = num_blocks;
-  a.ctx_limit = ctx_limit;
-  a.window = sliding_window;
-  a.scale = scale;
-  a.softcap = logit_softcap;
-  a.dtype = dtype;
-  return to_status(pa::launch_prefill(a, workspace, static_cast<hipStream_t>(stream)));
+  return prefill_impl(out, query, query_start_loc, num_q_tokens, max_query_len, key_cache,
+                      value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                      scale, logit_softcap, sliding_window, workspace, workspace_bytes, dtype, 0,
+                      1.f, 1.f, stream);
+}
+
+pa_status pa_prefill_chunk_fp8(void* out, const void* query, const int32_t* query_start_loc,
+                               int32_t num_q_tokens, int32_t max_query_len, const void* key_cache,
+                               const void* value_cache, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               int32_t max_context_len, float scale, float logit_softcap,
+                               int32_t sliding_window, float k_scale, float v_scale,
+                               void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                               void* stream) {
+  if (!valid_scale(k_scale) || !valid_scale(v_scale)) return PA_ERR_BAD_SHAPE;
+  return prefill_impl(out, query, query_start_loc, num_q_tokens, max_query_len, key_cache,
+                      value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                      scale, logit_softcap, sliding_window, workspace, workspace_bytes, dtype, 1,
+                      k_scale, v_scale, stream);
 }
 
 }  // extern "C"

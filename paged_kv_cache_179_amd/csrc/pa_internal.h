@@ -26,6 +26,9 @@ struct CacheWriteArgs {
   int32_t log2_block_size;
   int32_t num_blocks;
   int32_t elem_bytes;
+  int32_t src_dtype;  // key/value dtype (pa_dtype)
+  int32_t kv_fp8;     // quantise into E4M3 caches: byte = E4M3(key / k_scale), saturating
+  float k_scale, v_scale;
 };
 
 // Whole-block copies from one or two source pools to destination pools of the
@@ -66,7 +69,9 @@ struct DecodeArgs {
   int32_t window;          // sliding window (tokens attended, ending at the query); 0 = whole context
   float scale;
   float softcap;           // logit soft-cap; 0 = none
-  pa_dtype dtype;
+  pa_dtype dtype;          // query, output (and cache unless kv_fp8)
+  int32_t kv_fp8;          // caches hold E4M3 bytes, value = byte * k_scale (v_scale)
+  float k_scale, v_scale;
 };
 
 struct DecodeWorkspace {
@@ -98,7 +103,9 @@ struct PrefillArgs {
   int32_t window;  // sliding window (keys attended, ending at the row's own position); 0 = none
   float scale;
   float softcap;   // logit soft-cap; 0 = none
-  pa_dtype dtype;
+  pa_dtype dtype;  // query, output (and cache unless kv_fp8)
+  int32_t kv_fp8;  // caches hold E4M3 bytes, value = byte * k_scale (v_scale)
+  float k_scale, v_scale;
 };
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);

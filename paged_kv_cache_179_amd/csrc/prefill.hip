@@ -47,6 +47,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -74,6 +75,12 @@ struct Mma<BF16> {
     const bf16x2 r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
     return __builtin_bit_cast(unsigned, r);
   }
+  // Two E4M3 values (low or high half of w) as an exact bf16 pair.
+  template <bool HIGH>
+  __device__ static inline unsigned from_fp8(unsigned w) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
+    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+  }
 };
 template <>
 struct Mma<F16> {
@@ -85,6 +92,12 @@ struct Mma<F16> {
   __device__ static inline unsigned pack(float lo, float hi) {
     const f16x2 r = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
     return __builtin_bit_cast(unsigned, r);
+  }
+  // Two E4M3 values as an exact fp16 pair.
+  template <bool HIGH>
+  __device__ static inline unsigned from_fp8(unsigned w) {
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(f[0], f[1]));
   }
 };
 
@@ -177,7 +190,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
   }
 }
 
-template <typename E, int D, typename S>
+template <typename E, int D, typename S, bool KV8>
 __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs a, int32_t group,
                                                           int32_t pos_per_tile, int32_t nsplit,
                                                           const int4* plan, const int32_t* plan_count,
@@ -191,14 +204,19 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   constexpr int WAVES = prefill_threads(D) / 64;
   constexpr int RPW = 16 * NTW;              // rows per wave
   constexpr int WKEYS = kKeyTile / WAVES;    // keys each wave copies per pass
-  static_assert(WKEYS % RPI == 0, "a wave copies whole DMA instructions");
-  constexpr int NDW = 2 * (WKEYS / RPI);    // DMA instructions per wave per pass (K and V)
+  static_assert(KV8 || WKEYS % RPI == 0, "a wave copies whole DMA instructions");
+  // Cached rows: 2 D bytes (16-bit) or D bytes (E4M3, converted in LDS into
+  // the 16-bit tile the MFMAs read).
+  constexpr int CNC = KV8 ? NC / 2 : NC;                 // 16-byte chunks per cached row
+  constexpr int NDK = (WKEYS * CNC + 63) / 64;          // DMA instructions per wave per pass, K or V
+  constexpr int NDW = 2 * NDK;                          // ... K and V
   constexpr int KB = D / 32;            // k-steps of the score product
   constexpr int MT = D / 16;            // 16-dim output tiles
   // [buffer][K or V][key][chunk]; NBUF - 1 passes in flight ahead of the one
   // computed (at head_dim 256 the 8-wave workgroup has the CU to itself).
   constexpr int NBUF = D == 256 ? 4 : 3;
-  __shared__ u32x4 s_kv[NBUF][2][kKeyTile][NC];
+  __shared__ u32x4 s_kv[NBUF][2][kKeyTile][CNC];
+  __shared__ u32x4 s_cv[KV8 ? 2 : 1][kKeyTile][KV8 ? NC : 1];  // converted pass (E4M3 caches)
 
   // Item blockIdx.x / Hkv of the plan (longest first), for KV head blockIdx.x % Hkv.
   const int j = static_cast<int>(blockIdx.x) / a.num_kv_heads;
@@ -265,6 +283,27 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
     const int k0 = key_lo + p * kKeyTile + wave * WKEYS;
     const char* kd = reinterpret_cast<const char*>(&s_kv[b][0][wave * WKEYS][0]);
     const char* vd = reinterpret_cast<const char*>(&s_kv[b][1][wave * WKEYS][0]);
+    if constexpr (KV8) {
+      // E4M3 rows (D bytes) land unrotated, WKEYS * CNC 16-byte pieces per
+      // wave: the conversion applies the rotations.  Lanes past the wave's
+      // pieces sit out (an instruction still counts once in vmcnt).
+#pragma unroll
+      for (int r = 0; r < NDK; ++r) {
+        const int piece = r * 64 + lane;
+        if (piece < WKEYS * CNC) {
+          const int key = min(k0 + piece / CNC, key_hi - 1);
+          int blk = (1 << lbs) >= WKEYS ? tables[trow + (min(k0, key_hi - 1) >> lbs)]
+                                        : a.block_tables[trow + (key >> lbs)];
+          blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+          const int64_t roff =
+              (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * D +
+              (piece % CNC) * 16;
+          dma16(kbase + roff, kd + r * 1024);
+          dma16(vbase + roff, vd + r * 1024);
+        }
+      }
+      return;
+    }
     if ((1 << lbs) >= WKEYS) {
       // The wave's keys lie in one block: one scalar table read.
       int blk = tables[trow + (min(k0, key_hi - 1) >> lbs)];
@@ -323,8 +362,9 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
 
   auto compute = [&](int p, int b) {
     const int k0 = key_lo + p * kKeyTile;
-    const char* kt = reinterpret_cast<const char*>(&s_kv[b][0][0][0]);
-    const char* vt = reinterpret_cast<const char*>(&s_kv[b][1][0][0]);
+    const char* kt = KV8 ? reinterpret_cast<const char*>(&s_cv[0][0][0])
+                         : reinterpret_cast<const char*>(&s_kv[b][0][0][0]);
+    const char* vt = kt + kKeyTile * RB;
     // S^T of the pass: s[h][t] holds keys k0 + 16 h + 4 g4 + i of row 16 t + hl.
     f32x4 s[2][NTW];
 #pragma unroll
@@ -393,6 +433,28 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       default: wait_vmcnt<0>(); break;
     }
     __syncthreads();  // every wave's share of pass p has landed
+    if constexpr (KV8) {
+      // All threads turn the pass's E4M3 K and V rows into the rotated 16-bit
+      // tile; the next iteration's first barrier keeps it until every wave is
+      // done with it.
+      const int b = p % NBUF;
+#pragma unroll
+      for (int i = 0; i < 2 * kKeyTile * CNC / (64 * WAVES); ++i) {
+        const int idx = static_cast<int>(threadIdx.x) + i * 64 * WAVES;
+        const int kv = idx / (kKeyTile * CNC);
+        const int t = (idx / CNC) % kKeyTile;
+        const int c = 2 * (idx % CNC);
+        const u32x4 w = s_kv[b][kv][t][idx % CNC];
+        const u32x4 lo = {M::template from_fp8<false>(w[0]), M::template from_fp8<true>(w[0]),
+                          M::template from_fp8<false>(w[1]), M::template from_fp8<true>(w[1])};
+        const u32x4 hi = {M::template from_fp8<false>(w[2]), M::template from_fp8<true>(w[2]),
+                          M::template from_fp8<false>(w[3]), M::template from_fp8<true>(w[3])};
+        const int rot = kv == 0 ? rot_k(t) : rot_v(t);
+        s_cv[kv][t][(c - rot) & (NC - 1)] = lo;
+        s_cv[kv][t][(c + 1 - rot) & (NC - 1)] = hi;
+      }
+      __syncthreads();
+    }
     const int k0 = key_lo + p * kKeyTile;
     if (k0 <= wave_last && k0 + kKeyTile > wave_first) compute(p, p % NBUF);  // wave-uniform skip
   }
@@ -404,6 +466,10 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
     const int nsplit_row = row_lim[t] / kSplitKeys - max(row_lo[t], 0) / kSplitKeys + 1;
     const int64_t out_row = (static_cast<int64_t>(q_begin) + pos0 + rpos[t]) * a.num_heads + kvh * group + rhead[t];
     // Output register i of tile mt holds dim 16 mt + 4 g4 + i.
+    if constexpr (KV8) {  // values were read without their scale
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] *= a.v_scale;
+    }
     if (nsplit_row == 1) {
       const float inv = 1.f / lsum;
 #pragma unroll
@@ -498,10 +564,17 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
                      nsplit, plan, plan_count);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  with_score_map(a.scale, a.softcap, a.window, [&](auto map) {
-    hipLaunchKernelGGL((prefill_kernel<E, D, decltype(map)>), dim3(static_cast<uint32_t>(n)),
-                       dim3(prefill_threads(D)), 0, stream, a, group, pos_per_tile, nsplit, plan,
-                       plan_count, map, ws_max, ws_sum, ws_acc);
+  // An E4M3 cache's K scale folds into the score scale.
+  const float qk_scale = a.kv_fp8 ? a.scale * a.k_scale : a.scale;
+  with_score_map(qk_scale, a.softcap, a.window, [&](auto map) {
+    if (a.kv_fp8)
+      hipLaunchKernelGGL((prefill_kernel<E, D, decltype(map), true>), dim3(static_cast<uint32_t>(n)),
+                         dim3(prefill_threads(D)), 0, stream, a, group, pos_per_tile, nsplit, plan,
+                         plan_count, map, ws_max, ws_sum, ws_acc);
+    else
+      hipLaunchKernelGGL((prefill_kernel<E, D, decltype(map), false>), dim3(static_cast<uint32_t>(n)),
+                         dim3(prefill_threads(D)), 0, stream, a, group, pos_per_tile, nsplit, plan,
+                         plan_count, map, ws_max, ws_sum, ws_acc);
     return 0;
   });
   err = hipGetLastError();

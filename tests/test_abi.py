@@ -110,6 +110,33 @@ def test_block_ops_validation(lib):
     assert swap_blocks(lib, n=0, src=N, dst=N, m=N) == OK
 
 
+def test_fp8_validation(lib):
+    w8 = lambda n=4, dt=BF16, ks=0.1, vs=0.1, key=P, kc=P, d=64: lib.pa_reshape_and_cache_fp8(
+        key, P, kc, P, P, n, 2, d, 16, 8, dt, ks, vs, N)
+    assert w8(ks=0.0) == SHAPE
+    assert w8(vs=-1.0) == SHAPE
+    assert w8(ks=float("inf")) == SHAPE
+    assert w8(ks=float("nan")) == SHAPE
+    assert w8(dt=7) == UNSUP
+    assert w8(d=80) == UNSUP
+    assert w8(key=N) == NULLP
+    assert w8(kc=ctypes.c_void_p((1 << 20) + 8)) == UNSUP
+    assert w8(n=0, key=N, kc=N) == OK
+    dec8 = lambda fn="pa_decode_fp8", dt=F16, ks=0.1, vs=0.1, ws=P, s=4: getattr(lib, fn)(
+        P, P, P, P, P, 100, P, s, 8, 2, 128, 16, 64, 1000, 0.1, 0.0, 0, 512, ks, vs, ws, 1 << 30, dt, N)
+    for fn in ("pa_decode_fp8", "pa_decode_partitions_fp8"):
+        assert dec8(fn, dt=F32) == UNSUP  # fp8 caches need a 16-bit query
+        assert dec8(fn, ks=0.0) == SHAPE
+        assert dec8(fn, vs=float("nan")) == SHAPE
+        assert dec8(fn, ws=N) == NULLP
+        assert dec8(fn, s=0) == OK
+    pre8 = lambda ks=0.1, dt=BF16: lib.pa_prefill_chunk_fp8(
+        P, P, P, 64, 32, P, P, P, 8, P, 2, 8, 1, 256, 16, 64, 100, 0.1, 0.0, 0, ks, 0.1, P,
+        1 << 30, dt, N)
+    assert pre8(ks=-0.1) == SHAPE
+    assert pre8(dt=F32) == UNSUP
+
+
 def decode(lib, fn="pa_decode", out=P, q=P, kc=P, vc=P, bt=P, mbps=100, cl=P, s=4, hq=8, hkv=2,
            d=128, bs=16, nb=64, maxc=1000, scale=0.1, cap=0.0, win=0, part=512, ws=P,
            wsb=1 << 30, dt=F16):
