@@ -453,6 +453,57 @@ def variants(dev, cap=50.0, window=1024, reps=10):
             "prefill_mfma_frac": flops / (ms_p * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
+def fp8_kv(dev, names=("llama2_7b", "qwen25_7b"), reps=10):
+    """Decode over E4M3 (fp8) copies of the workloads' caches: the same step
+    with half the cache bytes.  The pools are converted once, outside the
+    timing (per-tensor scale 1/64: N(0, 1) values stay inside E4M3's range).
+    Bytes count each unique attended token's fp8 K and V once, plus Q, output
+    and table entries, as for the 16-bit line."""
+    from paged_kv_cache_179_amd import workloads as W
+
+    out = {}
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    scale = 1.0 / 64
+    for name in names:
+        w = W.make(name)
+        st = Step(w, dev)
+        st.write()
+        kc8 = (st.kc.float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+        vc8 = (st.vc.float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+        wk = work(w)
+        fp8_bytes = wk["decode_bytes"] - wk["decode_kv_bytes"] // 2  # K/V at one byte per element
+
+        def dec():
+            st.pa.decode(st.out_d, st.q_d, kc8, vc8, st.bt_d, st.cl_d, w.scale, st.maxc_d,
+                         partition_size=w.partition_size, workspace=st.ws_d, k_scale=scale,
+                         v_scale=scale)
+
+        def dec16():
+            st.pa.decode(st.out_d, st.q_d, st.kc, st.vc, st.bt_d, st.cl_d, w.scale, st.maxc_d,
+                         partition_size=w.partition_size, workspace=st.ws_d)
+
+        ts = {}
+        for label, fn in (("fp8", dec), ("16bit", dec16)):
+            v = []
+            for i in range(reps + 2):
+                flush.zero_()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                if i >= 2:
+                    v.append(e0.elapsed_time(e1))
+            ts[label] = float(np.mean(v))
+        out[name] = {"decode_ms": round(ts["fp8"], 5), "decode_gbs": fp8_bytes / (ts["fp8"] * 1e-3) / 1e9,
+                     "decode_hbm_frac": fp8_bytes / (ts["fp8"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "decode_bytes": fp8_bytes, "decode_ms_16bit_same_run": round(ts["16bit"], 5),
+                     "speedup_vs_16bit": ts["16bit"] / ts["fp8"]}
+        del st, kc8, vc8
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -514,12 +565,14 @@ def main():
         del st
         torch.cuda.empty_cache()
 
-    extras, variant = {}, None
+    extras, variant, fp8 = {}, None, None
     if not args.only:
         extras = block_ops(dev)
         log("block ops: " + json.dumps(extras))
         variant = variants(dev)
         log("variants: " + json.dumps(variant))
+        fp8 = fp8_kv(dev)
+        log("fp8 kv: " + json.dumps(fp8))
     w, wk, t, r = headline
     part_ms = float(np.mean(t["partitions"]))
     achieved = wk["partition_kernel_bytes"] / (part_ms * 1e-3) / 1e9
@@ -553,6 +606,7 @@ def main():
         "workloads": {k: v for k, v in results.items() if not k.startswith("_")},
         "block_ops": extras or None,
         "variants": variant,
+        "fp8_kv_cache": fp8,
     }
     print(json.dumps(line), flush=True)
 
