@@ -236,6 +236,31 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
                            pa_dtype dtype, void* stream);
 
 /*
+ * Chunked prefill with the chunk's own cache write fused in (one call for a
+ * mixed step: decode rows are chunks of L = 1).  As pa_prefill_chunk, plus
+ * the chunk tokens' new K and V ([num_q_tokens][num_kv_heads][head_dim],
+ * `dtype`) and their int64 slot_mapping [num_q_tokens] (negative or outside
+ * the pool: not written).  The attention reads the chunk's own keys and
+ * values from `key`/`value` (never from the cache, so no part of the launch
+ * waits for another's write), and the kernel writes them into the caches as
+ * pa_reshape_and_cache would; after the call the caches and the output are
+ * those of pa_reshape_and_cache followed by pa_prefill_chunk.  context_lens
+ * still include the chunk.  16-bit caches only.  (wLLM PyPI page, "Features --
+ * Core engine": chunked prefill; mini-vLLM README, "End-to-end throughput vs
+ * baselines": the K/V write as one indexed assignment.)
+ */
+pa_status pa_prefill_chunk_fused(void* out, const void* query, const void* key, const void* value,
+                                 const int64_t* slot_mapping, const int32_t* query_start_loc,
+                                 int32_t num_q_tokens, int32_t max_query_len, void* key_cache,
+                                 void* value_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_context_len, float scale, float logit_softcap,
+                                 int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                                 pa_dtype dtype, void* stream);
+
+/*
  * fp8 KV cache.  The vLLM native-Windows build README lists fp8 among its
  * KV-cache compression options ("KV compression" column of its release
  * table); the pages say no more, so this is the usual form: each cached K and

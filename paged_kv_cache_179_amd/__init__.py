@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     library,
     library_path,
     prefill_chunk,
+    prefill_chunk_fused,
     prefill_workspace_bytes,
     reshape_and_cache,
     reshape_and_cache_fp8,

@@ -56,6 +56,10 @@ _SIGNATURES = {
     "pa_prefill_chunk_fp8": ([_c_ptr, _c_ptr, _c_ptr, _i32, _i32, _c_ptr, _c_ptr, _c_ptr, _i32,
                               _c_ptr, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32,
                               _f32, _f32, _c_ptr, _size, ctypes.c_int, _c_ptr], ctypes.c_int),
+    "pa_prefill_chunk_fused": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _i32, _c_ptr,
+                                _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32, _i32, _i32, _i32, _i32,
+                                _i32, _f32, _f32, _i32, _c_ptr, _size, ctypes.c_int, _c_ptr],
+                               ctypes.c_int),
     "pa_prefill_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _size),
     "pa_prefill_chunk": ([_c_ptr, _c_ptr, _c_ptr, _i32, _i32, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr,
                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _c_ptr, _size,
@@ -350,4 +354,46 @@ def prefill_chunk(out: torch.Tensor, query: torch.Tensor, query_start_loc: torch
         args += list(_scales(key_cache, k_scale, v_scale))
     st = getattr(library(), name)(*args, ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
     _check(name, st)
+    return ws
+
+
+def prefill_chunk_fused(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor,
+                        value: torch.Tensor, slot_mapping: torch.Tensor,
+                        query_start_loc: torch.Tensor, key_cache: torch.Tensor,
+                        value_cache: torch.Tensor, block_tables: torch.Tensor,
+                        context_lens: torch.Tensor, scale: float, max_query_len: int,
+                        max_context_len: int, workspace: Optional[torch.Tensor] = None,
+                        logit_softcap: float = 0.0, sliding_window: int = 0) -> None:
+    """prefill_chunk with the chunk's own cache write fused in: ``key``/``value``
+    [num_q_tokens, Hkv, D] are written at ``slot_mapping`` (int64 [num_q_tokens])
+    and attended directly; see pa_prefill_chunk_fused."""
+    nb, hkv, bs, d = _cache_dims(key_cache, value_cache)
+    dt = query.dtype
+    if key_cache.dtype != dt:
+        raise TypeError("the fused call takes 16-bit caches of the query's dtype")
+    if query.dim() != 3 or query.shape[2] != d or out.shape != query.shape:
+        raise ValueError("query/out must be [num_q_tokens, num_heads, head_dim]")
+    nq, hq = int(query.shape[0]), int(query.shape[1])
+    if key.shape != value.shape or tuple(key.shape) != (nq, hkv, d):
+        raise ValueError("key/value must be [num_q_tokens, num_kv_heads, head_dim]")
+    if tuple(slot_mapping.shape) != (nq,):
+        raise ValueError("slot_mapping must be [num_q_tokens]")
+    s = int(context_lens.shape[0])
+    if tuple(query_start_loc.shape) != (s + 1,):
+        raise ValueError("query_start_loc must be [num_seqs + 1]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    need = prefill_workspace_bytes(nq, s, hq, hkv, d, max_query_len, max_context_len)
+    ws, ws_ptr = _workspace(need, out, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = library().pa_prefill_chunk_fused(
+        _dev(out, "out", dt), _dev(query, "query", dt), _dev(key, "key", dt),
+        _dev(value, "value", dt), _dev(slot_mapping, "slot_mapping", torch.int64),
+        _dev(query_start_loc, "query_start_loc", torch.int32), nq, int(max_query_len),
+        _dev(key_cache, "key_cache"), _dev(value_cache, "value_cache"),
+        _dev(block_tables, "block_tables", torch.int32), int(block_tables.shape[1]),
+        _dev(context_lens, "context_lens", torch.int32), s, hq, hkv, d, bs, nb,
+        int(max_context_len), float(scale), float(logit_softcap), int(sliding_window), ws_ptr,
+        nbytes, PA_DTYPE[dt], _stream(out))
+    _check("pa_prefill_chunk_fused", st)
     return ws

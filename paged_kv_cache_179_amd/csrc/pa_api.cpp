@@ -161,8 +161,10 @@ pa_status prefill_impl(void* out, const void* query, const int32_t* query_start_
                            int32_t max_context_len, float scale, float logit_softcap,
                            int32_t sliding_window, void* workspace, size_t workspace_bytes,
                            pa_dtype dtype, int32_t kv_fp8, float k_scale, float v_scale,
-                           void* stream) {
+                           const void* new_key, const void* new_value,
+                           const int64_t* slot_mapping, void* stream) {
   if (num_q_tokens < 0 || max_query_len < 0) return PA_ERR_BAD_SHAPE;
+  const bool fused = new_key != nullptr || new_value != nullptr || slot_mapping != nullptr;
   if (!valid_variant(logit_softcap, sliding_window)) return PA_ERR_BAD_SHAPE;
   pa_status st = check_decode_shapes(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                      max_blocks_per_seq, num_blocks, max_context_len, 0, dtype);
@@ -176,6 +178,11 @@ pa_status prefill_impl(void* out, const void* query, const int32_t* query_start_
       !aligned(value_cache, 16) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
       !aligned(query_start_loc, 4))
     return PA_ERR_UNSUPPORTED;
+  if (fused) {
+    if (!new_key || !new_value || !slot_mapping) return PA_ERR_NULL_POINTER;
+    if (!aligned(new_key, 16) || !aligned(new_value, 16) || !aligned(slot_mapping, 8))
+      return PA_ERR_UNSUPPORTED;
+  }
   const int32_t ctx_limit = clamp_i32(
       std::min<int64_t>(max_context_len, static_cast<int64_t>(max_blocks_per_seq) * block_size));
   if (ctx_limit == 0) return PA_OK;
@@ -209,6 +216,10 @@ pa_status prefill_impl(void* out, const void* query, const int32_t* query_start_
   a.kv_fp8 = kv_fp8;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
+  a.new_key = new_key;
+  a.new_value = new_value;
+  a.slot_mapping = slot_mapping;
+  a.fused = fused ? 1 : 0;
   return to_status(pa::launch_prefill(a, workspace, static_cast<hipStream_t>(stream)));
 }
 
@@ -472,7 +483,25 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
                       value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                       num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
                       scale, logit_softcap, sliding_window, workspace, workspace_bytes, dtype, 0,
-                      1.f, 1.f, stream);
+                      1.f, 1.f, nullptr, nullptr, nullptr, stream);
+}
+
+pa_status pa_prefill_chunk_fused(void* out, const void* query, const void* key, const void* value,
+                                 const int64_t* slot_mapping, const int32_t* query_start_loc,
+                                 int32_t num_q_tokens, int32_t max_query_len, void* key_cache,
+                                 void* value_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_context_len, float scale, float logit_softcap,
+                                 int32_t sliding_window, void* workspace, size_t workspace_bytes,
+                                 pa_dtype dtype, void* stream) {
+  if (num_q_tokens > 0 && (!key || !value || !slot_mapping)) return PA_ERR_NULL_POINTER;
+  return prefill_impl(out, query, query_start_loc, num_q_tokens, max_query_len, key_cache,
+                      value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                      num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
+                      scale, logit_softcap, sliding_window, workspace, workspace_bytes, dtype, 0,
+                      1.f, 1.f, key, value, slot_mapping, stream);
 }
 
 pa_status pa_prefill_chunk_fp8(void* out, const void* query, const int32_t* query_start_loc,
@@ -490,7 +519,7 @@ pa_status pa_prefill_chunk_fp8(void* out, const void* query, const int32_t* quer
                       value_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
                       num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len,
                       scale, logit_softcap, sliding_window, workspace, workspace_bytes, dtype, 1,
-                      k_scale, v_scale, stream);
+                      k_scale, v_scale, nullptr, nullptr, nullptr, stream);
 }
 
 }  // extern "C"

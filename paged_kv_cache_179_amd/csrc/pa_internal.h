@@ -106,6 +106,13 @@ struct PrefillArgs {
   pa_dtype dtype;  // query, output (and cache unless kv_fp8)
   int32_t kv_fp8;  // caches hold E4M3 bytes, value = byte * k_scale (v_scale)
   float k_scale, v_scale;
+  // Fused write (fused != 0): the chunk tokens' own K/V ([num_q_tokens][Hkv][D])
+  // are read from new_key/new_value instead of the cache, and written into the
+  // cache at slot_mapping by the kernel.
+  const void* new_key;
+  const void* new_value;
+  const int64_t* slot_mapping;
+  int32_t fused;
 };
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);

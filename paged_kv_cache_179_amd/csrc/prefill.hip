@@ -273,6 +273,38 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   const int64_t trow = static_cast<int64_t>(seq) * a.max_blocks_per_seq;
   cint* tables = reinterpret_cast<cint*>(reinterpret_cast<uintptr_t>(a.block_tables));
 
+  // Fused write: keys from chunk_start on are the chunk's own tokens.  The
+  // workgroups read them from new_key/new_value (never from the cache, so no
+  // workgroup waits for another's write), and the workgroup of the tile's
+  // first key range writes the tile's tokens (this KV head) into the cache.
+  const bool fused = !KV8 && a.fused != 0;
+  const int chunk_start = ctx - qlen;
+  if (fused) {
+    const int first_key = a.window > 0 ? max(0, chunk_start + pos0 - a.window + 1) : 0;
+    if (split == first_key / kSplitKeys) {
+      const int64_t num_slots = static_cast<int64_t>(a.num_blocks) << lbs;
+      for (int i = tid; i < 2 * npos * NC; i += 64 * WAVES) {
+        const int kv = i / (npos * NC);
+        const int r = i - kv * npos * NC;
+        const int64_t tok = static_cast<int64_t>(q_begin) + pos0 + r / NC;
+        const int64_t slot = a.slot_mapping[tok];
+        if (slot < 0 || slot >= num_slots) continue;
+        const char* src = static_cast<const char*>(kv ? a.new_value : a.new_key) +
+                          (tok * a.num_kv_heads + kvh) * RB + (r % NC) * 16;
+        char* dst = const_cast<char*>(kv ? vbase : kbase) +
+                    ((((slot >> lbs) * a.num_kv_heads + kvh) << lbs) + (slot & off_mask)) * RB +
+                    (r % NC) * 16;
+        *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+      }
+      wait_vmcnt<0>();  // the DMA pipeline below counts only its own transfers
+    }
+  }
+  // Source row of key `key` (K or V): the chunk's input row or the cache row.
+  auto fused_row = [&](const void* in, int key) {
+    return static_cast<const char*>(in) +
+           ((static_cast<int64_t>(q_begin) + key - chunk_start) * a.num_kv_heads + kvh) * RB;
+  };
+
   // Rotation (in chunks) of key row r and value row r of a tile.
   auto rot_k = [](int r) { return r % NC; };
   auto rot_v = [](int r) { return D == 64 ? (r & ~1) % NC : (2 * r) % NC; };
@@ -315,8 +347,11 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
         const int pos = lane % NC;
         const int key = min(k0 + r * RPI + lane / NC, key_hi - 1);
         const int64_t roff = head_off + static_cast<int64_t>(key & off_mask) * RB;
-        dma16(kbase + roff + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
-        dma16(vbase + roff + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+        const bool own = fused && key >= chunk_start;
+        const char* ksrc = own ? fused_row(a.new_key, key) : kbase + roff;
+        const char* vsrc = own ? fused_row(a.new_value, key) : vbase + roff;
+        dma16(ksrc + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+        dma16(vsrc + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
       }
     } else {
 #pragma unroll
@@ -327,8 +362,11 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
         int blk = a.block_tables[trow + (key >> lbs)];
         blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
         const int64_t roff = (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * RB;
-        dma16(kbase + roff + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
-        dma16(vbase + roff + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+        const bool own = fused && key >= chunk_start;
+        const char* ksrc = own ? fused_row(a.new_key, key) : kbase + roff;
+        const char* vsrc = own ? fused_row(a.new_value, key) : vbase + roff;
+        dma16(ksrc + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+        dma16(vsrc + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
       }
     }
   };

@@ -137,6 +137,18 @@ def test_fp8_validation(lib):
     assert pre8(dt=F32) == UNSUP
 
 
+def test_fused_prefill_validation(lib):
+    f = lambda key=P, value=P, slots=P, nq=64, dt=BF16: lib.pa_prefill_chunk_fused(
+        P, P, key, value, slots, P, nq, 32, P, P, P, 8, P, 2, 8, 1, 256, 16, 64, 100, 0.1, 0.0, 0,
+        P, 1 << 30, dt, N)
+    assert f(key=N) == NULLP
+    assert f(slots=N) == NULLP
+    assert f(value=ctypes.c_void_p((1 << 20) + 8)) == UNSUP
+    assert f(slots=ctypes.c_void_p((1 << 20) + 4)) == UNSUP
+    assert f(dt=F32) == UNSUP
+    assert f(nq=0, key=N, value=N, slots=N) == OK
+
+
 def decode(lib, fn="pa_decode", out=P, q=P, kc=P, vc=P, bt=P, mbps=100, cl=P, s=4, hq=8, hkv=2,
            d=128, bs=16, nb=64, maxc=1000, scale=0.1, cap=0.0, win=0, part=512, ws=P,
            wsb=1 << 30, dt=F16):
