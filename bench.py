@@ -453,6 +453,56 @@ def variants(dev, cap=50.0, window=1024, reps=10):
             "prefill_mfma_frac": flops / (ms_p * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
+def unified_step(dev, reps=10):
+    """The Gemma-2B-like mixed step as one fused call (pa_prefill_chunk_fused
+    over the 4 chunks and the 124 decode rows as one-token chunks, with all
+    2,172 new tokens' cache writes), beside the separate path (write, prefill,
+    decode partitions and reduce) on the same data."""
+    from paged_kv_cache_179_amd import workloads as W
+
+    w = W.make("gemma_2b_mixed")
+    st = Step(w, dev)
+    st.write()
+    rows = np.concatenate([w.prefill_rows, w.decode_rows])
+    lens = np.concatenate([np.diff(w.query_start_loc), np.ones(len(w.decode_rows), dtype=np.int64)])
+    qsl = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(dev)
+    q = torch.cat([st.q_p, st.q_d]).contiguous()
+    out = torch.empty_like(q)
+    bt = torch.from_numpy(w.block_tables[rows]).to(dev)
+    cl = torch.from_numpy(w.context_lens[rows]).to(dev)
+    maxq, maxc = int(lens.max()), int(w.context_lens[rows].max())
+    ws = torch.empty(max(256, st.pa.prefill_workspace_bytes(int(lens.sum()), len(rows), w.num_heads,
+                                                            w.num_kv_heads, w.head_dim, maxq, maxc)),
+                     dtype=torch.uint8, device=dev)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+
+    def fused():
+        st.pa.prefill_chunk_fused(out, q, st.nk, st.nv, st.slots, qsl, st.kc, st.vc, bt, cl,
+                                  w.scale, maxq, maxc, workspace=ws)
+
+    def separate():
+        for _, fn in st.phases():
+            fn()
+
+    ts = {}
+    for label, fn in (("fused", fused), ("separate", separate)):
+        v = []
+        for i in range(reps + 2):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 2:
+                v.append(e0.elapsed_time(e1))
+        ts[label] = float(np.mean(v))
+    step_bytes = work(w)["step_bytes"]
+    return {"workload": "gemma_2b_mixed", "fused_call_ms": round(ts["fused"], 5),
+            "separate_ms": round(ts["separate"], 5), "fused_step_gbs": step_bytes / (ts["fused"] * 1e-3) / 1e9,
+            "launches_fused": 3, "launches_separate": 7}
+
+
 def fp8_kv(dev, names=("llama2_7b", "qwen25_7b"), reps=10):
     """Decode over E4M3 (fp8) copies of the workloads' caches: the same step
     with half the cache bytes.  The pools are converted once, outside the
@@ -565,7 +615,7 @@ def main():
         del st
         torch.cuda.empty_cache()
 
-    extras, variant, fp8 = {}, None, None
+    extras, variant, fp8, unified = {}, None, None, None
     if not args.only:
         extras = block_ops(dev)
         log("block ops: " + json.dumps(extras))
@@ -573,6 +623,8 @@ def main():
         log("variants: " + json.dumps(variant))
         fp8 = fp8_kv(dev)
         log("fp8 kv: " + json.dumps(fp8))
+        unified = unified_step(dev)
+        log("unified step: " + json.dumps(unified))
     w, wk, t, r = headline
     part_ms = float(np.mean(t["partitions"]))
     achieved = wk["partition_kernel_bytes"] / (part_ms * 1e-3) / 1e9
@@ -607,6 +659,7 @@ def main():
         "block_ops": extras or None,
         "variants": variant,
         "fp8_kv_cache": fp8,
+        "fused_mixed_step": unified,
     }
     print(json.dumps(line), flush=True)
 
