@@ -55,7 +55,6 @@ constexpr int kHeadTile = 16;   // query heads per workgroup (MFMA N)
 constexpr float kLazyMax = 8.f; // log2 of the largest unnormalised probability
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -79,13 +78,12 @@ struct Mma<BF16> {
     const bf16x2 r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
     return __builtin_bit_cast(unsigned, r);
   }
-  // Two E4M3 values (the low or high half of w) as a bf16 pair.  Exact: the
-  // hardware conversion gives the fp32 value, whose 4 significant bits all
-  // sit in the upper half that bf16 keeps.
+  // Two E4M3 values (the low or high half of w) as a bf16 pair, in one gfx950
+  // scaled conversion with scale 1.  Exact: every E4M3 value (4 significant
+  // bits, exponents -9..8) is a bf16 value.
   template <bool HIGH>
   __device__ static inline unsigned from_fp8(unsigned w) {
-    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
-    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HIGH));
   }
 };
 template <>
@@ -103,12 +101,11 @@ struct Mma<F16> {
     const f16x2 r = {static_cast<_Float16>(lo), static_cast<_Float16>(hi)};
     return __builtin_bit_cast(unsigned, r);
   }
-  // Two E4M3 values as an fp16 pair; every E4M3 value is an fp16 value, so
-  // the (truncating) packed conversion is exact.
+  // Two E4M3 values as an fp16 pair (scaled conversion, scale 1); every E4M3
+  // value is an fp16 value, so this is exact.
   template <bool HIGH>
   __device__ static inline unsigned from_fp8(unsigned w) {
-    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
-    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(f[0], f[1]));
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, HIGH));
   }
 };
 
@@ -168,26 +165,36 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   constexpr int CRPI = 1024 / CRB;             // cached rows per DMA instruction
   constexpr int NDMA = kTile / CRPI;           // DMA instructions per pass, K or V
   constexpr int NQ = kHeadTile * RB / 1024;  // DMA instructions per query tile
-  
-  // Per wave, two pipeline slots, each a key tile and a value tile of
-  // [kTile rows][NC chunks].  A slot is exactly one wave's partial output
+
+  // Per wave, NS pipeline slots, each a key tile and a value tile of
+  // [kTile rows][CNC chunks].  16-bit caches: two slots, one pass in flight
+  // while the other is computed; a slot is exactly one wave's partial output
   // [16 heads][D] in fp32, which is where that goes at the end of a unit.
-  __shared__ u32x4 s_kv[kWaves][2][2][kTile][CNC];
-  // E4M3 caches: each wave's converted K and V tile of the pass it computes,
-  // rotated as the 16-bit slots are; also where its partial output goes.
-  __shared__ u32x4 s_cv[KV8 ? kWaves : 1][2][kTile][KV8 ? NC : 1];
+  // E4M3 caches: a pass is half the bytes, so three slots keep two passes in
+  // flight (the bytes in flight per wave of the 16-bit kernel).
+  constexpr int NS = KV8 ? 3 : 2;
+  __shared__ u32x4 s_kv[kWaves][NS][2][kTile][CNC];
+  // E4M3 caches: each wave's value tile of the pass it computes, widened to
+  // 16 bits and rotated as the 16-bit value slots are (keys are widened in
+  // registers).  At the end of a unit it holds heads 0-7 of the wave's
+  // partial output, and a free slot heads 8-15.
+  __shared__ u32x4 s_cv[KV8 ? kWaves : 1][kTile][KV8 ? NC : 1];
   // Query tile of the current unit and of the next one.
   __shared__ u32x4 s_q[2][kHeadTile][NC];
   __shared__ float s_max[kWaves][kHeadTile];
   __shared__ float s_sum[kWaves][kHeadTile];
   __shared__ int s_part[kWaves];
-  static_assert((KV8 ? sizeof(s_cv[0]) : sizeof(s_kv[0][0])) == kHeadTile * D * sizeof(float),
+  static_assert(sizeof(s_kv[0][0]) == (KV8 ? kHeadTile / 2 : kHeadTile) * D * sizeof(float),
                 "partial output fills a slot");
-  // K and V tile a wave's MFMAs read for the pass in slot `sl`, and the place
-  // of its partial output.
-  auto kv_tile = [&](int w, int sl) -> char* {
-    if constexpr (KV8) return reinterpret_cast<char*>(&s_cv[w][0][0][0]);
-    return reinterpret_cast<char*>(&s_kv[w][sl][0][0][0]);
+  static_assert(!KV8 || sizeof(s_cv[0]) == kHeadTile / 2 * D * sizeof(float),
+                "half the partial output fills the value tile");
+  // Partial output row of wave w, head h, when the wave's free slot is `sl`.
+  auto part_row = [&](int w, int sl, int h) -> float* {
+    if constexpr (KV8) {
+      if (h < kHeadTile / 2) return reinterpret_cast<float*>(&s_cv[w][0][0]) + h * D;
+      return reinterpret_cast<float*>(&s_kv[w][sl][0][0][0]) + (h - kHeadTile / 2) * D;
+    }
+    return reinterpret_cast<float*>(&s_kv[w][sl][0][0][0]) + h * D;
   };
 
   const int tid = threadIdx.x;
@@ -242,6 +249,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   int koff[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) koff[kb] = hl * RB + ((4 * kb + g4 - G::rot_k(hl) + NC) % NC) * 16;
+  // E4M3 keys: lane (hl, g4) reads the 16 key bytes of dims 16 c ..+15,
+  // c = 4 j + g4, for the MFMA pair 2 j (dims ..+7) and 2 j + 1 (dims 8..15);
+  // the query operands of that pair are the matching 16-bit chunks 2 c and
+  // 2 c + 1.  Raw key rows are stored with chunk c at (c - rot8(t)) mod CNC,
+  // rot8(t) = t CNC / 16, so the 16 rows of a read cover all 64 banks.
+  int k8off[KB / 2 > 0 ? KB / 2 : 1];
+  if constexpr (KV8) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      koff[kb] = hl * RB + ((2 * (4 * (kb / 2) + g4) + (kb & 1) - G::rot_k(hl) + NC) % NC) * 16;
+#pragma unroll
+    for (int j = 0; j < KB / 2; ++j) k8off[j] = hl * CRB + ((4 * j + g4 - hl * CNC / 16 + CNC) % CNC) * 16;
+  }
   int voff[MT];
   {
     const int vrow = 4 * g4 + (hl >> 2);
@@ -260,10 +280,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     const char* vd = reinterpret_cast<const char*>(&s_kv[wave][sl][1][0][0]);
     const int64_t trow = static_cast<int64_t>(x.seq) * a.max_blocks_per_seq;
     if constexpr (KV8) {
-      // E4M3 rows land unrotated; the conversion applies the rotations.
+      // E4M3 key rows land rotated by rot8(row) (see k8off); value rows land
+      // unrotated, since the widening pass reads them in order.
 #pragma unroll
       for (int r = 0; r < NDMA; ++r) {
         const int row = r * CRPI + lane / CNC;
+        const int pos = lane % CNC;
         const int t = min(t0 + row, x.te - 1);
         int b;
         if (lbs >= 4) {
@@ -273,10 +295,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
         }
         b = (b < 0 || b >= a.num_blocks) ? 0 : b;
         const int64_t roff =
-            ((((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) | (t & off_mask)) * CRB) +
-            (lane % CNC) * 16;
-        dma16(kbase + roff, kd + r * 1024);
-        dma16(vbase + roff, vd + r * 1024);
+            (((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) | (t & off_mask)) * CRB;
+        dma16(kbase + roff + ((pos + row * CNC / 16) % CNC) * 16, kd + r * 1024);
+        dma16(vbase + roff + pos * 16, vd + r * 1024);
       }
       return;
     }
@@ -327,28 +348,29 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     }
   };
 
-  // E4M3 caches: convert this wave's pass in slot `sl` into its 16-bit tile.
-  // Lane l takes 16-byte chunks l, l + 64, ... (chunk q: row q / CNC, dims
-  // 16 (q % CNC) ..+15) and writes the two 16-bit chunks they become at their
-  // rotated places.
+  // 16 E4M3 values (one 16-byte chunk) as two 16-bit chunks: dims 0..7 and 8..15.
+  auto widen = [](const u32x4& w, u32x4& lo, u32x4& hi) {
+    lo = u32x4{M::template from_fp8<false>(w[0]), M::template from_fp8<true>(w[0]),
+               M::template from_fp8<false>(w[1]), M::template from_fp8<true>(w[1])};
+    hi = u32x4{M::template from_fp8<false>(w[2]), M::template from_fp8<true>(w[2]),
+               M::template from_fp8<false>(w[3]), M::template from_fp8<true>(w[3])};
+  };
+
+  // E4M3 caches: widen this wave's value tile in slot `sl` into its 16-bit
+  // tile.  Lane l takes 16-byte chunks l, l + 64, ... (chunk q: row q / CNC,
+  // dims 16 (q % CNC) ..+15) and writes the two 16-bit chunks they become at
+  // their rotated places.
   auto convert = [&](int sl) {
     if constexpr (KV8) {
 #pragma unroll
-      for (int kv = 0; kv < 2; ++kv) {
-#pragma unroll
-        for (int i = 0; i < kTile * CNC / 64; ++i) {
-          const int q = lane + 64 * i;
-          const int t = q / CNC;
-          const int c = 2 * (q % CNC);
-          const u32x4 w = s_kv[wave][sl][kv][t][q % CNC];
-          const u32x4 lo = {M::template from_fp8<false>(w[0]), M::template from_fp8<true>(w[0]),
-                            M::template from_fp8<false>(w[1]), M::template from_fp8<true>(w[1])};
-          const u32x4 hi = {M::template from_fp8<false>(w[2]), M::template from_fp8<true>(w[2]),
-                            M::template from_fp8<false>(w[3]), M::template from_fp8<true>(w[3])};
-          const int rot = kv == 0 ? G::rot_k(t) : G::rot_v(t);
-          s_cv[wave][kv][t][(c - rot + NC) % NC] = lo;
-          s_cv[wave][kv][t][(c + 1 - rot + NC) % NC] = hi;
-        }
+      for (int i = 0; i < kTile * CNC / 64; ++i) {
+        const int q = lane + 64 * i;
+        const int t = q / CNC;
+        const int c = 2 * (q % CNC);
+        u32x4 lo, hi;
+        widen(s_kv[wave][sl][1][t][q % CNC], lo, hi);
+        s_cv[wave][t][(c - G::rot_v(t) + NC) % NC] = lo;
+        s_cv[wave][t][(c + 1 - G::rot_v(t) + NC) % NC] = hi;
       }
       wave_lds_sync();
     }
@@ -361,15 +383,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
 
   auto compute = [&](const Unit& x, int k, int sl, int qb) {
     const int t0 = x.tb + (k * kWaves + wave) * kTile;
-    const char* kt = kv_tile(wave, sl);
-    const char* vt = kt + kTile * RB;
+    const char* kt = reinterpret_cast<const char*>(&s_kv[wave][sl][0][0][0]);
+    const char* vt = KV8 ? reinterpret_cast<const char*>(&s_cv[wave][0][0]) : kt + kTile * RB;
     const char* qt = reinterpret_cast<const char*>(&s_q[qb][0][0]);
 
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (KV8) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-      s = M::qk(*reinterpret_cast<const u32x4*>(kt + koff[kb]),
-                *reinterpret_cast<const u32x4*>(qt + koff[kb]), s);
+      for (int j = 0; j < KB / 2; ++j) {
+        u32x4 lo, hi;
+        widen(*reinterpret_cast<const u32x4*>(kt + k8off[j]), lo, hi);
+        s = M::qk(lo, *reinterpret_cast<const u32x4*>(qt + koff[2 * j]), s);
+        s = M::qk(hi, *reinterpret_cast<const u32x4*>(qt + koff[2 * j + 1]), s);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        s = M::qk(*reinterpret_cast<const u32x4*>(kt + koff[kb]),
+                  *reinterpret_cast<const u32x4*>(qt + koff[kb]), s);
+    }
 
     // Lane (hl, g4) holds head hl's scores of tokens t0 + 4 g4 + i.
     float sc[4];
@@ -400,12 +432,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   };
 
   // Merge of the four waves' partial states of unit x (slot `pr` of each
-  // wave holds its partial output) and the output or workspace writes.
+  // wave is free and holds its partial output, or half of it) and the output
+  // or workspace writes.
   auto finish = [&](const Unit& x, int pr) {
-    float* part_out = reinterpret_cast<float*>(kv_tile(wave, pr));
+    float* part_out = part_row(wave, pr, hl);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      *reinterpret_cast<f32x4*>(part_out + hl * D + 16 * mt + 4 * g4) = acc[mt];
+      *reinterpret_cast<f32x4*>(part_out + 16 * mt + 4 * g4) = acc[mt];
     if (lane < kHeadTile) {
       s_max[wave][hl] = m;
       s_sum[wave][hl] = lacc[0];
@@ -434,8 +467,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
       for (int w = 0; w < kWaves; ++w) {
         const float f = exp2_fast(mw[w] - mu);
         den = __builtin_fmaf(f, s_sum[w][h], den);
-        num += f * *reinterpret_cast<const f32x4*>(
-                       reinterpret_cast<const float*>(kv_tile(w, s_part[w])) + h * D + d);
+        num += f * *reinterpret_cast<const f32x4*>(part_row(w, s_part[w], h) + d);
       }
       if constexpr (KV8) num *= a.v_scale;  // values were read without their scale
       const int64_t row = static_cast<int64_t>(x.seq) * a.num_heads + x.h_first + h;
@@ -475,6 +507,74 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     wait_vmcnt<0>();
   }
   __syncthreads();
+  if constexpr (KV8) {
+    // Three slots.  A wave's passes, unit after unit, form one stream: pass i
+    // of the stream uses slot i mod 3, and up to two passes are in flight
+    // ahead of the one computed (reaching into the next unit at the end of
+    // this one, so the merge overlaps them too).  Each wait leaves in flight
+    // exactly the DMAs issued after the pass it waits for: two per later pass
+    // and, for wave 0, the query tile if it was issued after that pass.
+    int issued = 0, done = 0;  // passes of the stream issued, computed
+    int ic = 0, in = 0;        // passes of cur, of nxt issued
+    int isl = 0, csl = 0;      // slots of the next pass to issue, to compute
+    int q_after = 0;           // wave 0: passes issued before the last query tile
+    auto issue_next = [&]() -> bool {
+      if (ic < cur.mine) {
+        issue(cur, ic++, isl);
+      } else if (nxt.valid && in < nxt.mine) {
+        issue(nxt, in++, isl);
+      } else {
+        return false;
+      }
+      ++issued;
+      isl = isl == NS - 1 ? 0 : isl + 1;
+      return true;
+    };
+    // Waits until at most n DMAs are in flight (n a multiple of 2 NDMA; the
+    // query tile is NQ = 2 NDMA).
+    static_assert(NQ == 2 * NDMA, "query tile counts as one pass");
+    auto wait_upto = [](int n) {
+      if (n >= 6 * NDMA) wait_vmcnt<6 * NDMA>();
+      else if (n >= 4 * NDMA) wait_vmcnt<4 * NDMA>();
+      else if (n >= 2 * NDMA) wait_vmcnt<2 * NDMA>();
+      else wait_vmcnt<0>();
+    };
+    while (true) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+      m = -__builtin_inff();
+      if (wave == 0 && nxt.valid) {
+        issue_q(nxt, qb ^ 1);  // older than every pass of nxt
+        q_after = issued;
+      }
+      for (int k = 0; k < cur.mine; ++k) {
+        while (issued - done < NS && issue_next()) {
+        }
+        const int later = issued - done - 1;
+        wait_upto(2 * NDMA * later + (wave == 0 && q_after > done ? NQ : 0));
+        wave_lds_sync();
+        convert(csl);
+        compute(cur, k, csl, qb);
+        ++done;
+        csl = csl == NS - 1 ? 0 : csl + 1;
+      }
+      while (issued - done < NS - 1 && issue_next()) {
+      }
+      // The next query tile has landed before the merge's barrier.
+      if (wave == 0 && nxt.valid) wait_upto(2 * NDMA * (issued - q_after));
+      // At most the two slots from csl on are in flight; the one before is free.
+      finish(cur, csl == 0 ? NS - 1 : csl - 1);
+      if (!nxt.valid) break;
+      u += stride;
+      cur = nxt;
+      nxt = info(u + stride);
+      qb ^= 1;
+      ic = in;
+      in = 0;
+    }
+    return;
+  }
   int slot = 0;
   if (cur.mine > 0) issue(cur, 0, slot);
   while (true) {

@@ -47,7 +47,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -78,8 +77,7 @@ struct Mma<BF16> {
   // Two E4M3 values (low or high half of w) as an exact bf16 pair.
   template <bool HIGH>
   __device__ static inline unsigned from_fp8(unsigned w) {
-    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
-    return __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HIGH));
   }
 };
 template <>
@@ -96,8 +94,7 @@ struct Mma<F16> {
   // Two E4M3 values as an exact fp16 pair.
   template <bool HIGH>
   __device__ static inline unsigned from_fp8(unsigned w) {
-    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), HIGH);
-    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_pkrtz(f[0], f[1]));
+    return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, HIGH));
   }
 };
 
