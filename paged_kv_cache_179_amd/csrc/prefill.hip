@@ -249,6 +249,12 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   // Keys any row of this wave sees (wave-uniform): passes outside are skipped.
   const int wave_last = min(last_key, ctx - qlen + pos0 + min(npos - 1, (wave * RPW + RPW - 1) / group));
   const int wave_first = ctx - qlen + pos0 + (wave * RPW) / group - win + 1;
+  // Passes whose 32 keys every row of the wave sees need no mask: keys up to
+  // the smallest row limit, from the largest window start, below key_hi.
+  // (Rows past the chunk see no key when masked; unmasked they score zeros
+  // against their zero query and are never written.)
+  const int wave_min_lim = ctx - qlen + pos0 + (wave * RPW) / group;
+  const int wave_max_lo = ctx - qlen + pos0 + min(npos - 1, (wave * RPW + RPW - 1) / group) - win + 1;
 
   // B operands of the scores: lane (hl, g4) of tile t holds dims 32 kb + 8 g4 .. + 7.
   u32x4 q[NTW][KB];
@@ -413,18 +419,27 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
         for (int t = 0; t < NTW; ++t) s[h][t] = M::run(ka, q[t][kb], s[h][t]);
       }
     }
+    const bool full = k0 + kKeyTile - 1 <= wave_min_lim && k0 + kKeyTile <= key_hi &&
+                      (!S::kWindow || k0 >= wave_max_lo);  // wave-uniform
     u32x4 pb[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
       float sc[8];
+      if (full) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = k0 + 16 * h + 4 * g4 + i;
-          const bool in = (!S::kWindow || key >= row_lo[t]) && key <= row_lim[t] && key < key_hi;
-          sc[4 * h + i] = in ? score(s[h][t][i]) : -__builtin_inff();
-        }
+          for (int i = 0; i < 4; ++i) sc[4 * h + i] = score(s[h][t][i]);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = k0 + 16 * h + 4 * g4 + i;
+            const bool in = (!S::kWindow || key >= row_lo[t]) && key <= row_lim[t] && key < key_hi;
+            sc[4 * h + i] = in ? score(s[h][t][i]) : -__builtin_inff();
+          }
+      }
       float mx = sc[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
@@ -458,19 +473,20 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   const int npass = (key_hi - key_lo + kKeyTile - 1) / kKeyTile;
   for (int p = 0; p < NBUF - 1 && p < npass; ++p) issue(p, p);
   for (int p = 0; p < npass; ++p) {
-    __syncthreads();  // every wave is done with pass p - 1's buffer
-    if (p + NBUF - 1 < npass) issue(p + NBUF - 1, (p + NBUF - 1) % NBUF);
     // Wait for this wave's share of pass p: the passes issued after it may stay in flight.
-    switch (min(NBUF - 1, npass - 1 - p)) {
-      case 3: wait_vmcnt<3 * NDW>(); break;
+    static_assert(NBUF <= 4, "wait cases");
+    switch (min(NBUF - 2, npass - 1 - p)) {
       case 2: wait_vmcnt<2 * NDW>(); break;
       case 1: wait_vmcnt<NDW>(); break;
       default: wait_vmcnt<0>(); break;
     }
-    __syncthreads();  // every wave's share of pass p has landed
+    // Every wave's share of pass p has landed, and every wave is done with
+    // pass p - 1, whose buffer the next DMA reuses.
+    __syncthreads();
+    if (p + NBUF - 1 < npass) issue(p + NBUF - 1, (p + NBUF - 1) % NBUF);
     if constexpr (KV8) {
       // All threads turn the pass's E4M3 K and V rows into the rotated 16-bit
-      // tile; the next iteration's first barrier keeps it until every wave is
+      // tile; the next iteration's barrier keeps it until every wave is
       // done with it.
       const int b = p % NBUF;
 #pragma unroll
