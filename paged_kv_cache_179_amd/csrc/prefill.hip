@@ -107,8 +107,6 @@ __device__ inline float max_across_rows(float x) {
   return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
-typedef __attribute__((address_space(4))) const int32_t cint;
-
 // The chunk, row tile and key range of one item, and the keys its rows see.
 struct PrefillItem {
   int q_begin, qlen, ctx, pos0, npos, last_key, key_lo, key_hi;
@@ -267,14 +265,22 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
     for (int kb = 0; kb < KB; ++kb)
       q[t][kb] = row_ok[t] ? load16(qp + (32 * kb + 8 * g4) * 2) : u32x4{0u, 0u, 0u, 0u};
   }
-  wait_vmcnt<0>();  // once, before any DMA: no compiler wait inside the pass loop
 
   const int lbs = a.log2_block_size;
   const int off_mask = (1 << lbs) - 1;
   const char* kbase = static_cast<const char*>(a.key_cache);
   const char* vbase = static_cast<const char*>(a.value_cache);
   const int64_t trow = static_cast<int64_t>(seq) * a.max_blocks_per_seq;
-  cint* tables = reinterpret_cast<cint*>(reinterpret_cast<uintptr_t>(a.block_tables));
+  // Block of this wave's share of each pass, lane i holding pass i's (a key
+  // range has at most kSplitKeys / kKeyTile passes): read once here, so that
+  // the pass loop takes it with a lane read instead of a memory round trip.
+  static_assert(kSplitKeys / kKeyTile <= 64, "one lane per pass");
+  int blk_lane = 0;
+  if ((1 << lbs) >= WKEYS && lane * kKeyTile < key_hi - key_lo) {
+    blk_lane = a.block_tables[trow + (min(key_lo + lane * kKeyTile + wave * WKEYS, key_hi - 1) >> lbs)];
+    blk_lane = (blk_lane < 0 || blk_lane >= a.num_blocks) ? 0 : blk_lane;
+  }
+  wait_vmcnt<0>();  // once, before any DMA: no compiler wait inside the pass loop
 
   // Fused write: keys from chunk_start on are the chunk's own tokens.  The
   // workgroups read them from new_key/new_value (never from the cache, so no
@@ -327,7 +333,7 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
         const int piece = r * 64 + lane;
         if (piece < WKEYS * CNC) {
           const int key = min(k0 + piece / CNC, key_hi - 1);
-          int blk = (1 << lbs) >= WKEYS ? tables[trow + (min(k0, key_hi - 1) >> lbs)]
+          int blk = (1 << lbs) >= WKEYS ? __builtin_amdgcn_readlane(blk_lane, p)
                                         : a.block_tables[trow + (key >> lbs)];
           blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
           const int64_t roff =
@@ -340,8 +346,8 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       return;
     }
     if ((1 << lbs) >= WKEYS) {
-      // The wave's keys lie in one block: one scalar table read.
-      int blk = tables[trow + (min(k0, key_hi - 1) >> lbs)];
+      // The wave's keys lie in one block, read at the start.
+      int blk = __builtin_amdgcn_readlane(blk_lane, p);
       blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
       const int64_t head_off = ((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) * RB;
 #pragma unroll
