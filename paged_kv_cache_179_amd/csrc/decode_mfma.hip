@@ -281,23 +281,35 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     const int64_t trow = static_cast<int64_t>(x.seq) * a.max_blocks_per_seq;
     if constexpr (KV8) {
       // E4M3 key rows land rotated by rot8(row) (see k8off); value rows land
-      // unrotated, since the widening pass reads them in order.
-#pragma unroll
-      for (int r = 0; r < NDMA; ++r) {
-        const int row = r * CRPI + lane / CNC;
-        const int pos = lane % CNC;
-        const int t = min(t0 + row, x.te - 1);
-        int b;
-        if (lbs >= 4) {
-          b = tables[trow + (t0 >> lbs)];
-        } else {
-          b = a.block_tables[trow + (t >> lbs)];
-        }
+      // unrotated, since the widening pass reads them in order.  As below,
+      // the table read is a scalar load for blocks of 16 or more tokens: a
+      // vector load here would make every DMA wait for all earlier ones.
+      if (lbs >= 4) {
+        int b = tables[trow + (t0 >> lbs)];
         b = (b < 0 || b >= a.num_blocks) ? 0 : b;
-        const int64_t roff =
-            (((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) | (t & off_mask)) * CRB;
-        dma16(kbase + roff + ((pos + row * CNC / 16) % CNC) * 16, kd + r * 1024);
-        dma16(vbase + roff + pos * 16, vd + r * 1024);
+        const int64_t head_off = ((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) * CRB;
+#pragma unroll
+        for (int r = 0; r < NDMA; ++r) {
+          const int row = r * CRPI + lane / CNC;
+          const int pos = lane % CNC;
+          const int t = min(t0 + row, x.te - 1);
+          const int64_t roff = head_off + static_cast<int64_t>(t & off_mask) * CRB;
+          dma16(kbase + roff + ((pos + row * CNC / 16) % CNC) * 16, kd + r * 1024);
+          dma16(vbase + roff + pos * 16, vd + r * 1024);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < NDMA; ++r) {
+          const int row = r * CRPI + lane / CNC;
+          const int pos = lane % CNC;
+          const int t = min(t0 + row, x.te - 1);
+          int b = a.block_tables[trow + (t >> lbs)];
+          b = (b < 0 || b >= a.num_blocks) ? 0 : b;
+          const int64_t roff =
+              (((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) | (t & off_mask)) * CRB;
+          dma16(kbase + roff + ((pos + row * CNC / 16) % CNC) * 16, kd + r * 1024);
+          dma16(vbase + roff + pos * 16, vd + r * 1024);
+        }
       }
       return;
     }

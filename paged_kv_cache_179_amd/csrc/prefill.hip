@@ -328,19 +328,38 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       // E4M3 rows (D bytes) land unrotated, WKEYS * CNC 16-byte pieces per
       // wave: the conversion applies the rotations.  Lanes past the wave's
       // pieces sit out (an instruction still counts once in vmcnt).
+      // The block id comes from the lanes read at the start, or, for blocks
+      // smaller than the wave's share, from a vector load in a loop of its
+      // own (a vector load joined into this loop would make every DMA wait
+      // for all earlier ones).
+      if ((1 << lbs) >= WKEYS) {
+        const int blk = __builtin_amdgcn_readlane(blk_lane, p);
 #pragma unroll
-      for (int r = 0; r < NDK; ++r) {
-        const int piece = r * 64 + lane;
-        if (piece < WKEYS * CNC) {
-          const int key = min(k0 + piece / CNC, key_hi - 1);
-          int blk = (1 << lbs) >= WKEYS ? __builtin_amdgcn_readlane(blk_lane, p)
-                                        : a.block_tables[trow + (key >> lbs)];
-          blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-          const int64_t roff =
-              (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * D +
-              (piece % CNC) * 16;
-          dma16(kbase + roff, kd + r * 1024);
-          dma16(vbase + roff, vd + r * 1024);
+        for (int r = 0; r < NDK; ++r) {
+          const int piece = r * 64 + lane;
+          if (piece < WKEYS * CNC) {
+            const int key = min(k0 + piece / CNC, key_hi - 1);
+            const int64_t roff =
+                (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * D +
+                (piece % CNC) * 16;
+            dma16(kbase + roff, kd + r * 1024);
+            dma16(vbase + roff, vd + r * 1024);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < NDK; ++r) {
+          const int piece = r * 64 + lane;
+          if (piece < WKEYS * CNC) {
+            const int key = min(k0 + piece / CNC, key_hi - 1);
+            int blk = a.block_tables[trow + (key >> lbs)];
+            blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+            const int64_t roff =
+                (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * D +
+                (piece % CNC) * 16;
+            dma16(kbase + roff, kd + r * 1024);
+            dma16(vbase + roff, vd + r * 1024);
+          }
         }
       }
       return;
