@@ -21,7 +21,10 @@ Figures:
   roofline       the decode partition kernel alone: its algorithmic bytes / its
                  average event-timed duration, against 8 TB/s;
   cpu_baseline   the fp64 oracle (tests' reference implementation, untuned) on a
-                 bounded sample of the same workload, one host thread.
+                 bounded sample of the same workload, one host thread;
+  stream_probe   a bare streaming read (the library's probe kernel) and a torch
+                 copy on the same box, against the spec, and the partition
+                 kernel's rate against the read probe.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
        python bench.py --profile-kernel NAME    (a few launches, for rocprofv3)
@@ -352,6 +355,41 @@ def copy_probe(nbytes=1 << 30, launches=3):
     log(f"copied {nbytes} bytes x {launches}")
 
 
+def stream_probe(dev, reps=5):
+    """What this machine's HBM gives a bare streaming read, for context beside the
+    8 TB/s spec: the library's read probe over 4 GiB (non-temporal 16-byte
+    loads, eight per lane in flight), and torch's 2 GiB -> 2 GiB copy (read +
+    write bytes); each the best of `reps` event-timed launches after one
+    warm-up."""
+    import paged_kv_cache_179_amd as pa
+
+    x = torch.empty(1 << 30, dtype=torch.int32, device=dev).fill_(1)
+    sink = torch.empty((x.numel() * 4 + (256 << 10) - 1) // (256 << 10), dtype=torch.int32, device=dev)
+    a = torch.empty(1 << 31, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+
+    def best(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    t_read = best(lambda: pa.stream_read_probe(x, sink))
+    t_copy = best(lambda: b.copy_(a))
+    out = {"read_gbs": x.numel() * 4 / t_read / 1e9, "copy_gbs": 2 * a.numel() / t_copy / 1e9}
+    out["read_frac_of_spec"] = out["read_gbs"] / HBM_PEAK_GBS
+    out["copy_frac_of_spec"] = out["copy_gbs"] / HBM_PEAK_GBS
+    del x, sink, a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def block_ops(dev, reps=10):
     """Block-pool copies on Llama-2-7B-like blocks (32 KV heads x 16 tokens x
     128 dims, fp16: 128 KiB per block and pool): copy-on-write of 1024 blocks
@@ -615,7 +653,7 @@ def main():
         del st
         torch.cuda.empty_cache()
 
-    extras, variant, fp8, unified = {}, None, None, None
+    extras, variant, fp8, unified, probe = {}, None, None, None, None
     if not args.only:
         extras = block_ops(dev)
         log("block ops: " + json.dumps(extras))
@@ -625,9 +663,13 @@ def main():
         log("fp8 kv: " + json.dumps(fp8))
         unified = unified_step(dev)
         log("unified step: " + json.dumps(unified))
+        probe = stream_probe(dev)
+        log("stream probe: " + json.dumps(probe))
     w, wk, t, r = headline
     part_ms = float(np.mean(t["partitions"]))
     achieved = wk["partition_kernel_bytes"] / (part_ms * 1e-3) / 1e9
+    if probe:
+        probe["headline_partition_kernel_frac_of_read_probe"] = achieved / probe["read_gbs"]
     traffic = counter_traffic(HEADLINE)
     line = {
         "metric": METRIC,
@@ -660,6 +702,7 @@ def main():
         "variants": variant,
         "fp8_kv_cache": fp8,
         "fused_mixed_step": unified,
+        "stream_probe": probe,
     }
     print(json.dumps(line), flush=True)
 

@@ -135,6 +135,20 @@ pa_status pa_swap_blocks(const void* src_cache, void* dst_cache, const int64_t* 
                          int32_t dst_num_blocks, void* stream);
 
 /*
+ * Measurement aid, not part of the attention path: a plain streaming read of
+ * `bytes` of device memory with non-temporal 16-byte loads, to compare the
+ * kernels' HBM rates with what a bare read reaches on the same device.
+ * Workgroup w reads bytes [w * 262144, (w + 1) * 262144) and writes the XOR of
+ * their 32-bit words to sink[w].
+ *   src    device memory, 16-byte aligned; bytes > 0, a multiple of 16
+ *   sink   device memory, sink_words >= ceil(bytes / 262144) uint32 words
+ * Returns PA_ERR_BAD_SHAPE for a bad size and PA_ERR_WORKSPACE_TOO_SMALL for a
+ * short sink.
+ */
+pa_status pa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
+                               void* stream);
+
+/*
  * Workspace bytes pa_decode needs (0 only when num_seqs <= 0): the work plan,
  * 256 + 16 * num_seqs * P bytes with P = ceil(max_context_len /
  * partition_size) (1 when partition_size == 0 or the context fits one

@@ -20,5 +20,6 @@ from .binding import (  # noqa: F401
     prefill_workspace_bytes,
     reshape_and_cache,
     reshape_and_cache_fp8,
+    stream_read_probe,
     swap_blocks,
 )

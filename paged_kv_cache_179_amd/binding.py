@@ -36,6 +36,7 @@ _SIGNATURES = {
                        ctypes.c_int),
     "pa_swap_blocks": ([_c_ptr, _c_ptr, _c_ptr, _i32, ctypes.c_int64, _i32, _i32, _c_ptr],
                        ctypes.c_int),
+    "pa_stream_read_probe": ([_c_ptr, ctypes.c_int64, _c_ptr, ctypes.c_int64, _c_ptr], ctypes.c_int),
     "pa_decode_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32], _size),
     "pa_decode": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32, _i32, _i32,
                    _i32, _i32, _i32, _f32, _f32, _i32, _i32, _c_ptr, _size, ctypes.c_int, _c_ptr],
@@ -225,6 +226,19 @@ def swap_blocks(src: torch.Tensor, dst: torch.Tensor, block_mapping: torch.Tenso
                                   int(block_mapping.shape[0]), int(block_bytes), int(src.shape[0]),
                                   int(dst.shape[0]), _stream(gpu))
     _check("pa_swap_blocks", st)
+
+
+def stream_read_probe(src: torch.Tensor, sink: torch.Tensor) -> None:
+    """Measurement aid: a bare streaming read of ``src`` (a contiguous GPU
+    tensor of a multiple of 16 bytes); ``sink`` (int32 on the GPU, at least
+    one word per 256 KiB of ``src``) receives each 256 KiB span's XOR of 32-bit
+    words."""
+    if sink.dtype != torch.int32:
+        raise TypeError("sink must be int32")
+    nbytes = src.numel() * src.element_size()
+    st = library().pa_stream_read_probe(_dev(src, "src"), nbytes, _dev(sink, "sink"), sink.numel(),
+                                        _stream(src))
+    _check("pa_stream_read_probe", st)
 
 
 def decode_workspace_bytes(num_seqs: int, num_heads: int, head_dim: int, max_context_len: int,

@@ -55,7 +55,52 @@ __global__ __launch_bounds__(kThreads) void block_copy_kernel(BlockCopyArgs a, i
   }
 }
 
+// Streaming-read probe: workgroup w reads bytes [w kProbeSpan, (w + 1)
+// kProbeSpan) of the source with non-temporal 16-byte loads, eight per lane in
+// flight, and stores the XOR of all its 32-bit words to sink[w] (so the loads
+// cannot be dropped, and a test can check what was read).
+constexpr int kProbeUnroll = 8;
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                               uint32_t* __restrict__ sink) {
+  constexpr int64_t kSpan16 = kProbeSpan / 16;
+  const int64_t begin = static_cast<int64_t>(blockIdx.x) * kSpan16;
+  const int64_t end = begin + kSpan16 < n16 ? begin + kSpan16 : n16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t i0 = begin + threadIdx.x; i0 < end; i0 += kThreads * kProbeUnroll) {
+    u32x4 v[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      const int64_t i = i0 + u * kThreads;
+      v[u] = i < end ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u];
+  }
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) x ^= __shfl_xor(x, off, kWave);
+  __shared__ uint32_t s_x[kThreads / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) s_x[threadIdx.x / kWave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t y = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / kWave; ++w) y ^= s_x[w];
+    sink[blockIdx.x] = y;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  const int64_t grid = (bytes + kProbeSpan - 1) / kProbeSpan;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(src), n16, sink);
+  return hipGetLastError();
+}
 
 hipError_t launch_block_copy(const BlockCopyArgs& a, hipStream_t stream) {
   if (a.num_pairs <= 0 || a.num_pools <= 0 || a.block_bytes <= 0) return hipSuccess;

@@ -239,7 +239,7 @@ const char* pa_status_str(int status) {
   }
 }
 
-int pa_version(void) { return 102; }
+int pa_version(void) { return 103; }
 
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                void* value_cache, const int64_t* slot_mapping,
@@ -302,6 +302,15 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, const int64_t* bloc
   a.src_blocks = num_blocks;
   a.dst_blocks = num_blocks;
   return to_status(pa::launch_block_copy(a, static_cast<hipStream_t>(stream)));
+}
+
+pa_status pa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, int64_t sink_words,
+                               void* stream) {
+  if (bytes <= 0 || bytes % 16 != 0 || sink_words < 0) return PA_ERR_BAD_SHAPE;
+  if (!src || !sink) return PA_ERR_NULL_POINTER;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return PA_ERR_UNSUPPORTED;
+  if (sink_words < (bytes + pa::kProbeSpan - 1) / pa::kProbeSpan) return PA_ERR_WORKSPACE_TOO_SMALL;
+  return to_status(pa::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
 }
 
 pa_status pa_swap_blocks(const void* src_cache, void* dst_cache, const int64_t* block_mapping,

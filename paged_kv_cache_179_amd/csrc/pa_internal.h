@@ -117,6 +117,9 @@ struct PrefillArgs {
 
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_block_copy(const BlockCopyArgs& a, hipStream_t stream);
+// Bytes each workgroup of the streaming-read probe reads (one sink word each).
+constexpr int64_t kProbeSpan = 256 * 1024;
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
 // 16-bit caches: the MFMA kernel (decode_mfma.hip), any group size.
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);

@@ -110,6 +110,17 @@ def test_block_ops_validation(lib):
     assert swap_blocks(lib, n=0, src=N, dst=N, m=N) == OK
 
 
+def test_stream_probe_validation(lib):
+    probe = lib.pa_stream_read_probe
+    assert probe(P, 0, P, 1, N) == SHAPE
+    assert probe(P, 24, P, 1, N) == SHAPE  # not a multiple of 16
+    assert probe(P, 16, P, -1, N) == SHAPE
+    assert probe(N, 16, P, 1, N) == NULLP
+    assert probe(P, 16, N, 1, N) == NULLP
+    assert probe(ctypes.c_void_p((1 << 20) + 8), 16, P, 1, N) == UNSUP
+    assert probe(P, (256 << 10) + 16, P, 1, N) == WS  # two spans, one sink word
+
+
 def test_fp8_validation(lib):
     w8 = lambda n=4, dt=BF16, ks=0.1, vs=0.1, key=P, kc=P, d=64: lib.pa_reshape_and_cache_fp8(
         key, P, kc, P, P, n, 2, d, 16, 8, dt, ks, vs, N)
