@@ -243,27 +243,51 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reduce_kernel(DecodeArg
   const int p1 = (ctx - 1) / a.part_tokens + 1;
   if (p1 - p0 <= 1) return;  // written by the partition kernel
   const int64_t base = static_cast<int64_t>(row) * a.num_parts;
-
-  float mx = -__builtin_inff();
-  for (int p = p0 + lane; p < p1; p += kWave) mx = fmaxf(mx, a.ws_max[base + p]);
-  mx = across_groups_max<1>(mx);
-  const float mu = safe_max(mx);
-  float den = 0.f;
-  for (int p = p0 + lane; p < p1; p += kWave) den += exp2_fast(a.ws_max[base + p] - mu) * a.ws_sum[base + p];
-  den = across_groups_sum<1>(den);
-
-  float num[PER];
+  typedef float vecf __attribute__((ext_vector_type(PER)));
+  vecf num = {};
+  float den;
+  if (p1 - p0 <= kWave) {
+    // One partition per lane: the max, the weights and the denominator come
+    // from one load per lane, and the partial outputs of the live partitions
+    // (a partition joined to an earlier one's work item holds no state: max
+    // -inf, sum 0, output never written) are read four at a time, their loads
+    // issued before any of them is used.
+    const bool in = lane < p1 - p0;
+    const float m_l = in ? a.ws_max[base + p0 + lane] : -__builtin_inff();
+    const float s_l = in ? a.ws_sum[base + p0 + lane] : 0.f;
+    const float mu = safe_max(across_groups_max<1>(m_l));
+    const float f_l = m_l == -__builtin_inff() ? 0.f : exp2_fast(m_l - mu);
+    den = across_groups_sum<1>(f_l * s_l);
+    uint64_t live = __builtin_amdgcn_ballot_w64(m_l != -__builtin_inff());
+    while (live != 0) {  // wave-uniform
+      int q[4];
+      float f[4];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) num[j] = 0.f;
-  for (int p = p0; p < p1; ++p) {
-    const float m = a.ws_max[base + p];
-    // A partition joined to an earlier one's work item holds no state: its
-    // max is -inf, its sum 0, and its partial output was never written.
-    if (m == -__builtin_inff()) continue;
-    const float f = exp2_fast(m - mu);
-    const float* src = a.ws_acc + (base + p) * D + lane * PER;
+      for (int i = 0; i < 4; ++i) {
+        q[i] = live != 0 ? __builtin_ctzll(live) : q[0];  // a live one again, weight 0
+        f[i] = live != 0 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(f_l), q[i])) : 0.f;
+        live &= live - 1;
+      }
+      vecf v[4];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) num[j] = __builtin_fmaf(f, src[j], num[j]);
+      for (int i = 0; i < 4; ++i)
+        v[i] = *reinterpret_cast<const vecf*>(a.ws_acc + (base + p0 + q[i]) * D + lane * PER);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) num += f[i] * v[i];
+    }
+  } else {
+    float mx = -__builtin_inff();
+    for (int p = p0 + lane; p < p1; p += kWave) mx = fmaxf(mx, a.ws_max[base + p]);
+    mx = across_groups_max<1>(mx);
+    const float mu = safe_max(mx);
+    den = 0.f;
+    for (int p = p0 + lane; p < p1; p += kWave) den += exp2_fast(a.ws_max[base + p] - mu) * a.ws_sum[base + p];
+    den = across_groups_sum<1>(den);
+    for (int p = p0; p < p1; ++p) {
+      const float m = a.ws_max[base + p];
+      if (m == -__builtin_inff()) continue;  // a joined partition: no state
+      num += exp2_fast(m - mu) * *reinterpret_cast<const vecf*>(a.ws_acc + (base + p) * D + lane * PER);
+    }
   }
 #pragma unroll
   for (int j = 0; j < PER; ++j)
