@@ -541,12 +541,13 @@ def unified_step(dev, reps=10):
             "launches_fused": 3, "launches_separate": 7}
 
 
-def fp8_kv(dev, names=("llama2_7b", "qwen25_7b"), reps=10):
-    """Decode over E4M3 (fp8) copies of the workloads' caches: the same step
-    with half the cache bytes.  The pools are converted once, outside the
-    timing (per-tensor scale 1/64: N(0, 1) values stay inside E4M3's range).
-    Bytes count each unique attended token's fp8 K and V once, plus Q, output
-    and table entries, as for the 16-bit line."""
+def fp8_kv(dev, names=("llama2_7b", "qwen25_7b", "gemma_2b_mixed"), reps=10):
+    """Decode (and, for the mixed workload, the prefill chunks) over E4M3 (fp8)
+    copies of the workloads' caches: the same step with half the cache bytes.
+    The pools are converted once, outside the timing (per-tensor scale 1/64:
+    N(0, 1) values stay inside E4M3's range).  Bytes count each unique
+    attended token's fp8 K and V once, plus Q, output and table entries, as for
+    the 16-bit line; prefill is counted in flops, as for the 16-bit line."""
     from paged_kv_cache_179_amd import workloads as W
 
     out = {}
@@ -570,8 +571,18 @@ def fp8_kv(dev, names=("llama2_7b", "qwen25_7b"), reps=10):
             st.pa.decode(st.out_d, st.q_d, st.kc, st.vc, st.bt_d, st.cl_d, w.scale, st.maxc_d,
                          partition_size=w.partition_size, workspace=st.ws_d)
 
+        def pre():
+            st.pa.prefill_chunk(st.out_p, st.q_p, st.qsl, kc8, vc8, st.bt_p, st.cl_p, w.scale,
+                                st.maxq, st.maxc_p, workspace=st.ws_p, k_scale=scale, v_scale=scale)
+
+        def pre16():
+            st.prefill()
+
+        fns = [("fp8", dec), ("16bit", dec16)]
+        if st.has_pre:
+            fns += [("pre_fp8", pre), ("pre_16bit", pre16)]
         ts = {}
-        for label, fn in (("fp8", dec), ("16bit", dec16)):
+        for label, fn in fns:
             v = []
             for i in range(reps + 2):
                 flush.zero_()
@@ -587,6 +598,11 @@ def fp8_kv(dev, names=("llama2_7b", "qwen25_7b"), reps=10):
                      "decode_hbm_frac": fp8_bytes / (ts["fp8"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "decode_bytes": fp8_bytes, "decode_ms_16bit_same_run": round(ts["16bit"], 5),
                      "speedup_vs_16bit": ts["16bit"] / ts["fp8"]}
+        if st.has_pre:
+            tf = wk["prefill_flops"] / (ts["pre_fp8"] * 1e-3) / 1e12
+            out[name].update({"prefill_ms": round(ts["pre_fp8"], 5), "prefill_tflops": tf,
+                              "prefill_mfma_frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                              "prefill_ms_16bit_same_run": round(ts["pre_16bit"], 5)})
         del st, kc8, vc8
         torch.cuda.empty_cache()
     return out
