@@ -198,9 +198,13 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache,
  * The two halves of pa_decode, for callers that time or schedule them apart
  * (pa_decode == pa_decode_partitions followed by pa_decode_reduce on the same
  * stream with the same arguments).  pa_decode_partitions writes the output of
- * every sequence that fits one partition and the partial softmax states of
- * the others into `workspace`; pa_decode_reduce merges those partial states
- * (log-sum-exp weighted) into `out` and leaves the other rows untouched.
+ * every sequence whose context one work item covers (one partition, or a run
+ * of up to four consecutive partitions that the work plan joins into one item
+ * when there are enough items to fill the device) and the partial softmax
+ * states of the others into `workspace`; pa_decode_reduce merges those partial
+ * states (log-sum-exp weighted) into `out` and leaves the other rows
+ * untouched.  The reduce reads the plan's choice from `workspace`, so it must
+ * get the workspace the partition call wrote.
  */
 pa_status pa_decode_partitions(void* out, const void* query, const void* key_cache,
                                const void* value_cache, const int32_t* block_tables,

@@ -241,7 +241,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reduce_kernel(DecodeArg
   // Partitions holding the attended tokens (the window's, or all of them).
   const int p0 = WIN ? window_start(a, ctx) / a.part_tokens : 0;
   const int p1 = (ctx - 1) / a.part_tokens + 1;
-  if (p1 - p0 <= 1) return;  // written by the partition kernel
+  // Rows whose partitions fit one work item were written by the partition kernel.
+  if (p1 - p0 <= (1 << a.plan_count[1])) return;
   const int64_t base = static_cast<int64_t>(row) * a.num_parts;
   typedef float vecf __attribute__((ext_vector_type(PER)));
   vecf num = {};
@@ -423,6 +424,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     hist[k_use][tid] = incl - c;
     if (tid == kWave - 1) {
       *a.plan_count = incl;
+      a.plan_count[1] = k_use;  // log2 of the span, for the reduce
       s_span = k_use;
     }
   }
@@ -434,7 +436,8 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     const int lo = WIN ? window_start(a, c) : 0;
     const int base = WIN ? first_part_token(lo) : 0;
     const int p0 = base > 0 ? base / P : 0;
-    const int single = c <= base + P ? 1 : 0;  // one partition: the output is final
+    // One item covers the sequence: its output is final, and the reduce skips the row.
+    const int single = c <= base + (P << k) ? 1 : 0;
     for (int slot = 0;; ++slot) {
       const int t = span_tokens(c, lo, base, k, slot);
       if (t <= 0) break;
@@ -507,6 +510,8 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_parts <= 1) return hipSuccess;
+  if (a.plan_count == nullptr || a.ws_max == nullptr || a.ws_sum == nullptr || a.ws_acc == nullptr)
+    return hipErrorInvalidValue;  // the kernel reads the plan's span and the partial states
   switch (a.dtype) {
     case PA_DTYPE_F32: return launch_reduce_e<F32>(a, stream);
     case PA_DTYPE_F16: return launch_reduce_e<F16>(a, stream);

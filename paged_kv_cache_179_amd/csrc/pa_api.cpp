@@ -393,6 +393,8 @@ pa_status pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_s
   a.ws_max = reinterpret_cast<float*>(const_cast<char*>(ws) + w.off_max);
   a.ws_sum = reinterpret_cast<float*>(const_cast<char*>(ws) + w.off_sum);
   a.ws_acc = reinterpret_cast<float*>(const_cast<char*>(ws) + w.off_acc);
+  // The partition call's plan: the reduce reads how many partitions an item joined.
+  a.plan_count = reinterpret_cast<int32_t*>(const_cast<char*>(ws) + w.off_count);
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.head_dim = head_dim;
