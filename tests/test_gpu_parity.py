@@ -106,6 +106,18 @@ def test_decode_joined_partitions(gpu, case):
     err = max_err(out, oracle_decode(w, kc, vc))
     say(f"  max abs err {err:.3e}")
     assert err <= TOL[dtype]
+    # The two halves: sequences one joined item covers are final after the
+    # partition call (the reduce leaves them alone); the reduce finishes the rest.
+    half = torch.full_like(out, float("nan"))
+    maxc = int(w.context_lens[w.decode_rows].max())
+    ws = pa.decode_partitions(half, d["query_decode"], d["key_cache"], d["value_cache"],
+                              d["bt_decode"], d["cl_decode"], w.scale, maxc, partition_size=64)
+    torch.cuda.synchronize()
+    short = w.context_lens[w.decode_rows] <= 64
+    assert not torch.isnan(half[torch.from_numpy(short)]).any(), "one-partition rows written"
+    pa.decode_reduce(half, d["cl_decode"], hq, d_, w.max_blocks_per_seq, w.block_size, maxc, 64, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, half)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
