@@ -61,6 +61,9 @@ constexpr int kRowsPerWg = 128;  // query rows sharing each K/V tile
 constexpr int prefill_row_tiles(int head_dim) { return head_dim == 256 ? 1 : 2; }
 constexpr int prefill_threads(int head_dim) { return kRowsPerWg / (16 * prefill_row_tiles(head_dim)) * 64; }
 constexpr int kKeyTile = 32;  // keys per pass
+// Head dims whose prefill launch is persistent (see prefill_kernel).
+template <int D>
+constexpr bool kPersistentPrefill = D == 256;
 constexpr int kSplitKeys = 1024;
 constexpr float kLazyMax = 8.f;
 
@@ -216,370 +219,377 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   __shared__ u32x4 s_kv[NBUF][2][kKeyTile][CNC];
   __shared__ u32x4 s_cv[KV8 ? 2 : 1][kKeyTile][KV8 ? NC : 1];  // converted pass (E4M3 caches)
 
-  // Persistent: workgroup b takes the plan's units (item, KV head) b, then
-  // 2G - 1 - b, then 2G + b, ... (G workgroups): the plan is longest first, so
-  // the workgroups that drew the shortest units of one round draw the longest
-  // of the next.  Launching one workgroup per unit instead left the last
-  // units waiting for the hardware to hand them a CU well after others had
-  // gone idle.
+  // At head_dim 256 (one 8-wave workgroup per CU) the launch is persistent:
+  // workgroup b takes the plan's units (item, KV head) b, then 2G - 1 - b, then
+  // 2G + b, ... (G workgroups).  The plan is longest first, so the workgroups
+  // that drew the shortest units of one round draw the longest of the next;
+  // one workgroup per unit left the last units waiting for the hardware to
+  // hand them a CU well after others had gone idle.  At smaller head dims,
+  // where several workgroups share a CU, one workgroup per unit is faster (the
+  // loop costs registers and so occupancy there).
   const int n_units = *plan_count * a.num_kv_heads;
-  for (int round = 0;; ++round) {
-    const int g = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
-    const int unit = round * g + ((round & 1) ? g - 1 - b : b);
-    if (unit >= n_units) break;  // units only grow with the round
-    [&] {
-      const int j = unit / a.num_kv_heads;
-      const int kvh = unit - j * a.num_kv_heads;
-      const int4 pi = plan[j];
-      const int seq = pi.x, split = pi.z;
-      const PrefillItem item = prefill_item(a, seq, pi.y, split, pos_per_tile);
-      if (!item.valid) return;
-      const int q_begin = item.q_begin, ctx = item.ctx, qlen = item.qlen, pos0 = item.pos0;
-      const int npos = item.npos, last_key = item.last_key, key_lo = item.key_lo, key_hi = item.key_hi;
+  auto run_unit = [&](const int unit) {
+    const int j = unit / a.num_kv_heads;
+    const int kvh = unit - j * a.num_kv_heads;
+    const int4 pi = plan[j];
+    const int seq = pi.x, split = pi.z;
+    const PrefillItem item = prefill_item(a, seq, pi.y, split, pos_per_tile);
+    if (!item.valid) return;
+    const int q_begin = item.q_begin, ctx = item.ctx, qlen = item.qlen, pos0 = item.pos0;
+    const int npos = item.npos, last_key = item.last_key, key_lo = item.key_lo, key_hi = item.key_hi;
 
-      const int tid = threadIdx.x;
-      const int lane = tid & 63;
-      const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-      const int hl = lane & 15;
-      const int g4 = lane >> 4;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hl = lane & 15;
+    const int g4 = lane >> 4;
 
-      // This lane's query rows (one per 16-row tile of the wave): the keys
-      // row_lo .. row_lim it attends (row_lo <= 0 without a window).
-      int row_lim[NTW], row_lo[NTW], rpos[NTW], rhead[NTW];
-      bool row_ok[NTW];
-      const int win = a.window > 0 ? a.window : 0x40000000;
+    // This lane's query rows (one per 16-row tile of the wave): the keys
+    // row_lo .. row_lim it attends (row_lo <= 0 without a window).
+    int row_lim[NTW], row_lo[NTW], rpos[NTW], rhead[NTW];
+    bool row_ok[NTW];
+    const int win = a.window > 0 ? a.window : 0x40000000;
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        const int row = wave * RPW + 16 * t + hl;
-        rpos[t] = row / group;
-        rhead[t] = row - rpos[t] * group;
-        row_ok[t] = rpos[t] < npos;
-        row_lim[t] = row_ok[t] ? ctx - qlen + pos0 + rpos[t] : -1;
-        row_lo[t] = row_lim[t] - win + 1;
-      }
-      // Keys any row of this wave sees (wave-uniform): passes outside are skipped.
-      const int wave_last = min(last_key, ctx - qlen + pos0 + min(npos - 1, (wave * RPW + RPW - 1) / group));
-      const int wave_first = ctx - qlen + pos0 + (wave * RPW) / group - win + 1;
-      // Passes whose 32 keys every row of the wave sees need no mask: keys up to
-      // the smallest row limit, from the largest window start, below key_hi.
-      // (Rows past the chunk see no key when masked; unmasked they score zeros
-      // against their zero query and are never written.)
-      const int wave_min_lim = ctx - qlen + pos0 + (wave * RPW) / group;
-      const int wave_max_lo = ctx - qlen + pos0 + min(npos - 1, (wave * RPW + RPW - 1) / group) - win + 1;
+    for (int t = 0; t < NTW; ++t) {
+      const int row = wave * RPW + 16 * t + hl;
+      rpos[t] = row / group;
+      rhead[t] = row - rpos[t] * group;
+      row_ok[t] = rpos[t] < npos;
+      row_lim[t] = row_ok[t] ? ctx - qlen + pos0 + rpos[t] : -1;
+      row_lo[t] = row_lim[t] - win + 1;
+    }
+    // Keys any row of this wave sees (wave-uniform): passes outside are skipped.
+    const int wave_last = min(last_key, ctx - qlen + pos0 + min(npos - 1, (wave * RPW + RPW - 1) / group));
+    const int wave_first = ctx - qlen + pos0 + (wave * RPW) / group - win + 1;
+    // Passes whose 32 keys every row of the wave sees need no mask: keys up to
+    // the smallest row limit, from the largest window start, below key_hi.
+    // (Rows past the chunk see no key when masked; unmasked they score zeros
+    // against their zero query and are never written.)
+    const int wave_min_lim = ctx - qlen + pos0 + (wave * RPW) / group;
+    const int wave_max_lo = ctx - qlen + pos0 + min(npos - 1, (wave * RPW + RPW - 1) / group) - win + 1;
 
-      // B operands of the scores: lane (hl, g4) of tile t holds dims 32 kb + 8 g4 .. + 7.
-      u32x4 q[NTW][KB];
+    // B operands of the scores: lane (hl, g4) of tile t holds dims 32 kb + 8 g4 .. + 7.
+    u32x4 q[NTW][KB];
 #pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        const char* qp = static_cast<const char*>(a.query) +
-                         ((static_cast<int64_t>(q_begin) + pos0 + (row_ok[t] ? rpos[t] : 0)) * a.num_heads +
-                          kvh * group + rhead[t]) * static_cast<int64_t>(RB);
+    for (int t = 0; t < NTW; ++t) {
+      const char* qp = static_cast<const char*>(a.query) +
+                       ((static_cast<int64_t>(q_begin) + pos0 + (row_ok[t] ? rpos[t] : 0)) * a.num_heads +
+                        kvh * group + rhead[t]) * static_cast<int64_t>(RB);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          q[t][kb] = row_ok[t] ? load16(qp + (32 * kb + 8 * g4) * 2) : u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int kb = 0; kb < KB; ++kb)
+        q[t][kb] = row_ok[t] ? load16(qp + (32 * kb + 8 * g4) * 2) : u32x4{0u, 0u, 0u, 0u};
+    }
 
-      const int lbs = a.log2_block_size;
-      const int off_mask = (1 << lbs) - 1;
-      const char* kbase = static_cast<const char*>(a.key_cache);
-      const char* vbase = static_cast<const char*>(a.value_cache);
-      const int64_t trow = static_cast<int64_t>(seq) * a.max_blocks_per_seq;
-      // Block of this wave's share of each pass, lane i holding pass i's (a key
-      // range has at most kSplitKeys / kKeyTile passes): read once here, so that
-      // the pass loop takes it with a lane read instead of a memory round trip.
-      static_assert(kSplitKeys / kKeyTile <= 64, "one lane per pass");
-      int blk_lane = 0;
-      if ((1 << lbs) >= WKEYS && lane * kKeyTile < key_hi - key_lo) {
-        blk_lane = a.block_tables[trow + (min(key_lo + lane * kKeyTile + wave * WKEYS, key_hi - 1) >> lbs)];
-        blk_lane = (blk_lane < 0 || blk_lane >= a.num_blocks) ? 0 : blk_lane;
-      }
-      wait_vmcnt<0>();  // once, before any DMA: no compiler wait inside the pass loop
+    const int lbs = a.log2_block_size;
+    const int off_mask = (1 << lbs) - 1;
+    const char* kbase = static_cast<const char*>(a.key_cache);
+    const char* vbase = static_cast<const char*>(a.value_cache);
+    const int64_t trow = static_cast<int64_t>(seq) * a.max_blocks_per_seq;
+    // Block of this wave's share of each pass, lane i holding pass i's (a key
+    // range has at most kSplitKeys / kKeyTile passes): read once here, so that
+    // the pass loop takes it with a lane read instead of a memory round trip.
+    static_assert(kSplitKeys / kKeyTile <= 64, "one lane per pass");
+    int blk_lane = 0;
+    if ((1 << lbs) >= WKEYS && lane * kKeyTile < key_hi - key_lo) {
+      blk_lane = a.block_tables[trow + (min(key_lo + lane * kKeyTile + wave * WKEYS, key_hi - 1) >> lbs)];
+      blk_lane = (blk_lane < 0 || blk_lane >= a.num_blocks) ? 0 : blk_lane;
+    }
+    wait_vmcnt<0>();  // once, before any DMA: no compiler wait inside the pass loop
 
-      // Fused write: keys from chunk_start on are the chunk's own tokens.  The
-      // workgroups read them from new_key/new_value (never from the cache, so no
-      // workgroup waits for another's write), and the workgroup of the tile's
-      // first key range writes the tile's tokens (this KV head) into the cache.
-      const bool fused = !KV8 && a.fused != 0;
-      const int chunk_start = ctx - qlen;
-      if (fused) {
-        const int first_key = a.window > 0 ? max(0, chunk_start + pos0 - a.window + 1) : 0;
-        if (split == first_key / kSplitKeys) {
-          const int64_t num_slots = static_cast<int64_t>(a.num_blocks) << lbs;
-          for (int i = tid; i < 2 * npos * NC; i += 64 * WAVES) {
-            const int kv = i / (npos * NC);
-            const int r = i - kv * npos * NC;
-            const int64_t tok = static_cast<int64_t>(q_begin) + pos0 + r / NC;
-            const int64_t slot = a.slot_mapping[tok];
-            if (slot < 0 || slot >= num_slots) continue;
-            const char* src = static_cast<const char*>(kv ? a.new_value : a.new_key) +
-                              (tok * a.num_kv_heads + kvh) * RB + (r % NC) * 16;
-            char* dst = const_cast<char*>(kv ? vbase : kbase) +
-                        ((((slot >> lbs) * a.num_kv_heads + kvh) << lbs) + (slot & off_mask)) * RB +
-                        (r % NC) * 16;
-            *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
-          }
-          wait_vmcnt<0>();  // the DMA pipeline below counts only its own transfers
+    // Fused write: keys from chunk_start on are the chunk's own tokens.  The
+    // workgroups read them from new_key/new_value (never from the cache, so no
+    // workgroup waits for another's write), and the workgroup of the tile's
+    // first key range writes the tile's tokens (this KV head) into the cache.
+    const bool fused = !KV8 && a.fused != 0;
+    const int chunk_start = ctx - qlen;
+    if (fused) {
+      const int first_key = a.window > 0 ? max(0, chunk_start + pos0 - a.window + 1) : 0;
+      if (split == first_key / kSplitKeys) {
+        const int64_t num_slots = static_cast<int64_t>(a.num_blocks) << lbs;
+        for (int i = tid; i < 2 * npos * NC; i += 64 * WAVES) {
+          const int kv = i / (npos * NC);
+          const int r = i - kv * npos * NC;
+          const int64_t tok = static_cast<int64_t>(q_begin) + pos0 + r / NC;
+          const int64_t slot = a.slot_mapping[tok];
+          if (slot < 0 || slot >= num_slots) continue;
+          const char* src = static_cast<const char*>(kv ? a.new_value : a.new_key) +
+                            (tok * a.num_kv_heads + kvh) * RB + (r % NC) * 16;
+          char* dst = const_cast<char*>(kv ? vbase : kbase) +
+                      ((((slot >> lbs) * a.num_kv_heads + kvh) << lbs) + (slot & off_mask)) * RB +
+                      (r % NC) * 16;
+          *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
         }
+        wait_vmcnt<0>();  // the DMA pipeline below counts only its own transfers
       }
-      // Source row of key `key` (K or V): the chunk's input row or the cache row.
-      auto fused_row = [&](const void* in, int key) {
-        return static_cast<const char*>(in) +
-               ((static_cast<int64_t>(q_begin) + key - chunk_start) * a.num_kv_heads + kvh) * RB;
-      };
+    }
+    // Source row of key `key` (K or V): the chunk's input row or the cache row.
+    auto fused_row = [&](const void* in, int key) {
+      return static_cast<const char*>(in) +
+             ((static_cast<int64_t>(q_begin) + key - chunk_start) * a.num_kv_heads + kvh) * RB;
+    };
 
-      // Rotation (in chunks) of key row r and value row r of a tile.
-      auto rot_k = [](int r) { return r % NC; };
-      auto rot_v = [](int r) { return D == 64 ? (r & ~1) % NC : (2 * r) % NC; };
+    // Rotation (in chunks) of key row r and value row r of a tile.
+    auto rot_k = [](int r) { return r % NC; };
+    auto rot_v = [](int r) { return D == 64 ? (r & ~1) % NC : (2 * r) % NC; };
 
-      // This wave's share of pass `p`'s DMA (keys 8 wave .. 8 wave + 7 of the
-      // pass) into buffer `b`.  Keys past the range are clamped to its last key.
-      auto issue = [&](int p, int b) {
-        const int k0 = key_lo + p * kKeyTile + wave * WKEYS;
-        const char* kd = reinterpret_cast<const char*>(&s_kv[b][0][wave * WKEYS][0]);
-        const char* vd = reinterpret_cast<const char*>(&s_kv[b][1][wave * WKEYS][0]);
-        if constexpr (KV8) {
-          // E4M3 rows (D bytes) land unrotated, WKEYS * CNC 16-byte pieces per
-          // wave: the conversion applies the rotations.  Lanes past the wave's
-          // pieces sit out (an instruction still counts once in vmcnt).
-          // The block id comes from the lanes read at the start, or, for blocks
-          // smaller than the wave's share, from a vector load in a loop of its
-          // own (a vector load joined into this loop would make every DMA wait
-          // for all earlier ones).
-          if ((1 << lbs) >= WKEYS) {
-            const int blk = __builtin_amdgcn_readlane(blk_lane, p);
-#pragma unroll
-            for (int r = 0; r < NDK; ++r) {
-              const int piece = r * 64 + lane;
-              if (piece < WKEYS * CNC) {
-                const int key = min(k0 + piece / CNC, key_hi - 1);
-                const int64_t roff =
-                    (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * D +
-                    (piece % CNC) * 16;
-                dma16(kbase + roff, kd + r * 1024);
-                dma16(vbase + roff, vd + r * 1024);
-              }
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < NDK; ++r) {
-              const int piece = r * 64 + lane;
-              if (piece < WKEYS * CNC) {
-                const int key = min(k0 + piece / CNC, key_hi - 1);
-                int blk = a.block_tables[trow + (key >> lbs)];
-                blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-                const int64_t roff =
-                    (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * D +
-                    (piece % CNC) * 16;
-                dma16(kbase + roff, kd + r * 1024);
-                dma16(vbase + roff, vd + r * 1024);
-              }
-            }
-          }
-          return;
-        }
+    // This wave's share of pass `p`'s DMA (keys 8 wave .. 8 wave + 7 of the
+    // pass) into buffer `b`.  Keys past the range are clamped to its last key.
+    auto issue = [&](int p, int b) {
+      const int k0 = key_lo + p * kKeyTile + wave * WKEYS;
+      const char* kd = reinterpret_cast<const char*>(&s_kv[b][0][wave * WKEYS][0]);
+      const char* vd = reinterpret_cast<const char*>(&s_kv[b][1][wave * WKEYS][0]);
+      if constexpr (KV8) {
+        // E4M3 rows (D bytes) land unrotated, WKEYS * CNC 16-byte pieces per
+        // wave: the conversion applies the rotations.  Lanes past the wave's
+        // pieces sit out (an instruction still counts once in vmcnt).
+        // The block id comes from the lanes read at the start, or, for blocks
+        // smaller than the wave's share, from a vector load in a loop of its
+        // own (a vector load joined into this loop would make every DMA wait
+        // for all earlier ones).
         if ((1 << lbs) >= WKEYS) {
-          // The wave's keys lie in one block, read at the start.
-          int blk = __builtin_amdgcn_readlane(blk_lane, p);
-          blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-          const int64_t head_off = ((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) * RB;
+          const int blk = __builtin_amdgcn_readlane(blk_lane, p);
 #pragma unroll
-          for (int r = 0; r < WKEYS / RPI; ++r) {
-            const int row = wave * WKEYS + r * RPI + lane / NC;  // row of the tile
-            const int pos = lane % NC;
-            const int key = min(k0 + r * RPI + lane / NC, key_hi - 1);
-            const int64_t roff = head_off + static_cast<int64_t>(key & off_mask) * RB;
-            const bool own = fused && key >= chunk_start;
-            const char* ksrc = own ? fused_row(a.new_key, key) : kbase + roff;
-            const char* vsrc = own ? fused_row(a.new_value, key) : vbase + roff;
-            dma16(ksrc + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
-            dma16(vsrc + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+          for (int r = 0; r < NDK; ++r) {
+            const int piece = r * 64 + lane;
+            if (piece < WKEYS * CNC) {
+              const int key = min(k0 + piece / CNC, key_hi - 1);
+              const int64_t roff =
+                  (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * D +
+                  (piece % CNC) * 16;
+              dma16(kbase + roff, kd + r * 1024);
+              dma16(vbase + roff, vd + r * 1024);
+            }
           }
         } else {
 #pragma unroll
-          for (int r = 0; r < WKEYS / RPI; ++r) {
-            const int row = wave * WKEYS + r * RPI + lane / NC;
-            const int pos = lane % NC;
-            const int key = min(k0 + r * RPI + lane / NC, key_hi - 1);
-            int blk = a.block_tables[trow + (key >> lbs)];
-            blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
-            const int64_t roff = (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * RB;
-            const bool own = fused && key >= chunk_start;
-            const char* ksrc = own ? fused_row(a.new_key, key) : kbase + roff;
-            const char* vsrc = own ? fused_row(a.new_value, key) : vbase + roff;
-            dma16(ksrc + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
-            dma16(vsrc + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+          for (int r = 0; r < NDK; ++r) {
+            const int piece = r * 64 + lane;
+            if (piece < WKEYS * CNC) {
+              const int key = min(k0 + piece / CNC, key_hi - 1);
+              int blk = a.block_tables[trow + (key >> lbs)];
+              blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+              const int64_t roff =
+                  (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * D +
+                  (piece % CNC) * 16;
+              dma16(kbase + roff, kd + r * 1024);
+              dma16(vbase + roff, vd + r * 1024);
+            }
           }
         }
-      };
+        return;
+      }
+      if ((1 << lbs) >= WKEYS) {
+        // The wave's keys lie in one block, read at the start.
+        int blk = __builtin_amdgcn_readlane(blk_lane, p);
+        blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+        const int64_t head_off = ((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) * RB;
+#pragma unroll
+        for (int r = 0; r < WKEYS / RPI; ++r) {
+          const int row = wave * WKEYS + r * RPI + lane / NC;  // row of the tile
+          const int pos = lane % NC;
+          const int key = min(k0 + r * RPI + lane / NC, key_hi - 1);
+          const int64_t roff = head_off + static_cast<int64_t>(key & off_mask) * RB;
+          const bool own = fused && key >= chunk_start;
+          const char* ksrc = own ? fused_row(a.new_key, key) : kbase + roff;
+          const char* vsrc = own ? fused_row(a.new_value, key) : vbase + roff;
+          dma16(ksrc + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+          dma16(vsrc + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < WKEYS / RPI; ++r) {
+          const int row = wave * WKEYS + r * RPI + lane / NC;
+          const int pos = lane % NC;
+          const int key = min(k0 + r * RPI + lane / NC, key_hi - 1);
+          int blk = a.block_tables[trow + (key >> lbs)];
+          blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
+          const int64_t roff = (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * RB;
+          const bool own = fused && key >= chunk_start;
+          const char* ksrc = own ? fused_row(a.new_key, key) : kbase + roff;
+          const char* vsrc = own ? fused_row(a.new_value, key) : vbase + roff;
+          dma16(ksrc + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+          dma16(vsrc + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+        }
+      }
+    };
 
-      // Per-lane LDS offsets (bytes within one K or V tile), as a row base and a
-      // rotated chunk position; NC is a power of two.
-      //   keys: row 16 h + hl, chunk 4 kb + g4;
-      //   values (transposing reads): row 16 h + 4 g4 + hl / 4, dims 16 mt + 4 (hl % 4).
-      static_assert((NC & (NC - 1)) == 0, "chunk count is a power of two");
-      const int vrow0 = 4 * g4 + (hl >> 2);
-      const int q4 = hl & 3;
-      const int vpos0 = (q4 >> 1) - rot_v(vrow0);  // row 16 + vrow0: rotation + 32, the same mod NC
-      auto koff = [&](int h, int kb) {
-        return (16 * h + hl) * RB + ((g4 - rot_k(16 * h + hl) + 4 * kb) & (NC - 1)) * 16;
-      };
-      auto voff = [&](int h, int mt) {
-        return (16 * h + vrow0) * RB + ((vpos0 + 2 * mt) & (NC - 1)) * 16 + (q4 & 1) * 8;
-      };
+    // Per-lane LDS offsets (bytes within one K or V tile), as a row base and a
+    // rotated chunk position; NC is a power of two.
+    //   keys: row 16 h + hl, chunk 4 kb + g4;
+    //   values (transposing reads): row 16 h + 4 g4 + hl / 4, dims 16 mt + 4 (hl % 4).
+    static_assert((NC & (NC - 1)) == 0, "chunk count is a power of two");
+    const int vrow0 = 4 * g4 + (hl >> 2);
+    const int q4 = hl & 3;
+    const int vpos0 = (q4 >> 1) - rot_v(vrow0);  // row 16 + vrow0: rotation + 32, the same mod NC
+    auto koff = [&](int h, int kb) {
+      return (16 * h + hl) * RB + ((g4 - rot_k(16 * h + hl) + 4 * kb) & (NC - 1)) * 16;
+    };
+    auto voff = [&](int h, int mt) {
+      return (16 * h + vrow0) * RB + ((vpos0 + 2 * mt) & (NC - 1)) * 16 + (q4 & 1) * 8;
+    };
 
-      const u32x4 ones = {M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair};
-      f32x4 acc[NTW][MT];
-      f32x4 lacc[NTW];
-      float m[NTW];
+    const u32x4 ones = {M::kOnePair, M::kOnePair, M::kOnePair, M::kOnePair};
+    f32x4 acc[NTW][MT];
+    f32x4 lacc[NTW];
+    float m[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m[t] = -__builtin_inff();
+    }
+
+    auto compute = [&](int p, int b) {
+      const int k0 = key_lo + p * kKeyTile;
+      const char* kt = KV8 ? reinterpret_cast<const char*>(&s_cv[0][0][0])
+                           : reinterpret_cast<const char*>(&s_kv[b][0][0][0]);
+      const char* vt = kt + kKeyTile * RB;
+      // S^T of the pass: s[h][t] holds keys k0 + 16 h + 4 g4 + i of row 16 t + hl.
+      f32x4 s[2][NTW];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) s[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + koff(h, kb));
+#pragma unroll
+          for (int t = 0; t < NTW; ++t) s[h][t] = M::run(ka, q[t][kb], s[h][t]);
+        }
+      }
+      const bool full = k0 + kKeyTile - 1 <= wave_min_lim && k0 + kKeyTile <= key_hi &&
+                        (!S::kWindow || k0 >= wave_max_lo);  // wave-uniform
+      u32x4 pb[NTW];
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
+        float sc[8];
+        if (full) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        m[t] = -__builtin_inff();
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[4 * h + i] = score(s[h][t][i]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = k0 + 16 * h + 4 * g4 + i;
+              const bool in = (!S::kWindow || key >= row_lo[t]) && key <= row_lim[t] && key < key_hi;
+              sc[4 * h + i] = in ? score(s[h][t][i]) : -__builtin_inff();
+            }
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
+        mx = max_across_rows(mx);
+        if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyMax) != 0) {  // wave-uniform
+          const float m_new = fmaxf(m[t], mx);
+          const float alpha = exp2_fast(m[t] - safe_max(m_new));
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[t][mt] *= alpha;
+          lacc[t] *= alpha;
+          m[t] = m_new;
+        }
+        const float mu = safe_max(m[t]);
+        pb[t] = u32x4{M::pack(exp2_fast(sc[0] - mu), exp2_fast(sc[1] - mu)),
+                      M::pack(exp2_fast(sc[2] - mu), exp2_fast(sc[3] - mu)),
+                      M::pack(exp2_fast(sc[4] - mu), exp2_fast(sc[5] - mu)),
+                      M::pack(exp2_fast(sc[6] - mu), exp2_fast(sc[7] - mu))};
+        lacc[t] = M::run(ones, pb[t], lacc[t]);
       }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        const u32x2 v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(0, mt))));
+        const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(1, mt))));
+        const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[t][mt] = M::run(va, pb[t], acc[t][mt]);
+      }
+    };
 
-      auto compute = [&](int p, int b) {
-        const int k0 = key_lo + p * kKeyTile;
-        const char* kt = KV8 ? reinterpret_cast<const char*>(&s_cv[0][0][0])
-                             : reinterpret_cast<const char*>(&s_kv[b][0][0][0]);
-        const char* vt = kt + kKeyTile * RB;
-        // S^T of the pass: s[h][t] holds keys k0 + 16 h + 4 g4 + i of row 16 t + hl.
-        f32x4 s[2][NTW];
+    const int npass = (key_hi - key_lo + kKeyTile - 1) / kKeyTile;
+    for (int p = 0; p < NBUF - 1 && p < npass; ++p) issue(p, p);
+    for (int p = 0; p < npass; ++p) {
+      // Wait for this wave's share of pass p: the passes issued after it may stay in flight.
+      static_assert(NBUF <= 4, "wait cases");
+      switch (min(NBUF - 2, npass - 1 - p)) {
+        case 2: wait_vmcnt<2 * NDW>(); break;
+        case 1: wait_vmcnt<NDW>(); break;
+        default: wait_vmcnt<0>(); break;
+      }
+      // Every wave's share of pass p has landed, and every wave is done with
+      // pass p - 1, whose buffer the next DMA reuses.
+      __syncthreads();
+      if (p + NBUF - 1 < npass) issue(p + NBUF - 1, (p + NBUF - 1) % NBUF);
+      if constexpr (KV8) {
+        // All threads turn the pass's E4M3 K and V rows into the rotated 16-bit
+        // tile; the next iteration's barrier keeps it until every wave is
+        // done with it.
+        const int b = p % NBUF;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int t = 0; t < NTW; ++t) s[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + koff(h, kb));
-#pragma unroll
-            for (int t = 0; t < NTW; ++t) s[h][t] = M::run(ka, q[t][kb], s[h][t]);
-          }
+        for (int i = 0; i < 2 * kKeyTile * CNC / (64 * WAVES); ++i) {
+          const int idx = static_cast<int>(threadIdx.x) + i * 64 * WAVES;
+          const int kv = idx / (kKeyTile * CNC);
+          const int t = (idx / CNC) % kKeyTile;
+          const int c = 2 * (idx % CNC);
+          const u32x4 w = s_kv[b][kv][t][idx % CNC];
+          const u32x4 lo = {M::template from_fp8<false>(w[0]), M::template from_fp8<true>(w[0]),
+                            M::template from_fp8<false>(w[1]), M::template from_fp8<true>(w[1])};
+          const u32x4 hi = {M::template from_fp8<false>(w[2]), M::template from_fp8<true>(w[2]),
+                            M::template from_fp8<false>(w[3]), M::template from_fp8<true>(w[3])};
+          const int rot = kv == 0 ? rot_k(t) : rot_v(t);
+          s_cv[kv][t][(c - rot) & (NC - 1)] = lo;
+          s_cv[kv][t][(c + 1 - rot) & (NC - 1)] = hi;
         }
-        const bool full = k0 + kKeyTile - 1 <= wave_min_lim && k0 + kKeyTile <= key_hi &&
-                          (!S::kWindow || k0 >= wave_max_lo);  // wave-uniform
-        u32x4 pb[NTW];
+        __syncthreads();
+      }
+      const int k0 = key_lo + p * kKeyTile;
+      if (k0 <= wave_last && k0 + kKeyTile > wave_first) compute(p, p % NBUF);  // wave-uniform skip
+    }
+
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-          float sc[8];
-          if (full) {
+    for (int t = 0; t < NTW; ++t) {
+      if (!row_ok[t] || key_lo > row_lim[t] || key_hi <= row_lo[t]) continue;  // no key of this range for this row
+      const float lsum = lacc[t][0];
+      const int nsplit_row = row_lim[t] / kSplitKeys - max(row_lo[t], 0) / kSplitKeys + 1;
+      const int64_t out_row = (static_cast<int64_t>(q_begin) + pos0 + rpos[t]) * a.num_heads + kvh * group + rhead[t];
+      // Output register i of tile mt holds dim 16 mt + 4 g4 + i.
+      if constexpr (KV8) {  // values were read without their scale
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) sc[4 * h + i] = score(s[h][t][i]);
-          } else {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int key = k0 + 16 * h + 4 * g4 + i;
-                const bool in = (!S::kWindow || key >= row_lo[t]) && key <= row_lim[t] && key < key_hi;
-                sc[4 * h + i] = in ? score(s[h][t][i]) : -__builtin_inff();
-              }
-          }
-          float mx = sc[0];
-#pragma unroll
-          for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-          mx = max_across_rows(mx);
-          if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyMax) != 0) {  // wave-uniform
-            const float m_new = fmaxf(m[t], mx);
-            const float alpha = exp2_fast(m[t] - safe_max(m_new));
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[t][mt] *= alpha;
-            lacc[t] *= alpha;
-            m[t] = m_new;
-          }
-          const float mu = safe_max(m[t]);
-          pb[t] = u32x4{M::pack(exp2_fast(sc[0] - mu), exp2_fast(sc[1] - mu)),
-                        M::pack(exp2_fast(sc[2] - mu), exp2_fast(sc[3] - mu)),
-                        M::pack(exp2_fast(sc[4] - mu), exp2_fast(sc[5] - mu)),
-                        M::pack(exp2_fast(sc[6] - mu), exp2_fast(sc[7] - mu))};
-          lacc[t] = M::run(ones, pb[t], lacc[t]);
-        }
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] *= a.v_scale;
+      }
+      if (nsplit_row == 1) {
+        const float inv = 1.f / lsum;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-          const u32x2 v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(0, mt))));
-          const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(1, mt))));
-          const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
-#pragma unroll
-          for (int t = 0; t < NTW; ++t) acc[t][mt] = M::run(va, pb[t], acc[t][mt]);
+          const f32x4 o = acc[t][mt] * inv;
+          const u32x2 packed = {M::pack(o[0], o[1]), M::pack(o[2], o[3])};
+          *reinterpret_cast<u32x2*>(static_cast<char*>(a.out) + (out_row * D + 16 * mt + 4 * g4) * 2) = packed;
         }
-      };
-
-      const int npass = (key_hi - key_lo + kKeyTile - 1) / kKeyTile;
-      for (int p = 0; p < NBUF - 1 && p < npass; ++p) issue(p, p);
-      for (int p = 0; p < npass; ++p) {
-        // Wait for this wave's share of pass p: the passes issued after it may stay in flight.
-        static_assert(NBUF <= 4, "wait cases");
-        switch (min(NBUF - 2, npass - 1 - p)) {
-          case 2: wait_vmcnt<2 * NDW>(); break;
-          case 1: wait_vmcnt<NDW>(); break;
-          default: wait_vmcnt<0>(); break;
-        }
-        // Every wave's share of pass p has landed, and every wave is done with
-        // pass p - 1, whose buffer the next DMA reuses.
-        __syncthreads();
-        if (p + NBUF - 1 < npass) issue(p + NBUF - 1, (p + NBUF - 1) % NBUF);
-        if constexpr (KV8) {
-          // All threads turn the pass's E4M3 K and V rows into the rotated 16-bit
-          // tile; the next iteration's barrier keeps it until every wave is
-          // done with it.
-          const int b = p % NBUF;
+      } else {
+        const int64_t ws = out_row * nsplit + split;
 #pragma unroll
-          for (int i = 0; i < 2 * kKeyTile * CNC / (64 * WAVES); ++i) {
-            const int idx = static_cast<int>(threadIdx.x) + i * 64 * WAVES;
-            const int kv = idx / (kKeyTile * CNC);
-            const int t = (idx / CNC) % kKeyTile;
-            const int c = 2 * (idx % CNC);
-            const u32x4 w = s_kv[b][kv][t][idx % CNC];
-            const u32x4 lo = {M::template from_fp8<false>(w[0]), M::template from_fp8<true>(w[0]),
-                              M::template from_fp8<false>(w[1]), M::template from_fp8<true>(w[1])};
-            const u32x4 hi = {M::template from_fp8<false>(w[2]), M::template from_fp8<true>(w[2]),
-                              M::template from_fp8<false>(w[3]), M::template from_fp8<true>(w[3])};
-            const int rot = kv == 0 ? rot_k(t) : rot_v(t);
-            s_cv[kv][t][(c - rot) & (NC - 1)] = lo;
-            s_cv[kv][t][(c + 1 - rot) & (NC - 1)] = hi;
-          }
-          __syncthreads();
-        }
-        const int k0 = key_lo + p * kKeyTile;
-        if (k0 <= wave_last && k0 + kKeyTile > wave_first) compute(p, p % NBUF);  // wave-uniform skip
-      }
-
-#pragma unroll
-      for (int t = 0; t < NTW; ++t) {
-        if (!row_ok[t] || key_lo > row_lim[t] || key_hi <= row_lo[t]) continue;  // no key of this range for this row
-        const float lsum = lacc[t][0];
-        const int nsplit_row = row_lim[t] / kSplitKeys - max(row_lo[t], 0) / kSplitKeys + 1;
-        const int64_t out_row = (static_cast<int64_t>(q_begin) + pos0 + rpos[t]) * a.num_heads + kvh * group + rhead[t];
-        // Output register i of tile mt holds dim 16 mt + 4 g4 + i.
-        if constexpr (KV8) {  // values were read without their scale
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[t][mt] *= a.v_scale;
-        }
-        if (nsplit_row == 1) {
-          const float inv = 1.f / lsum;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 o = acc[t][mt] * inv;
-            const u32x2 packed = {M::pack(o[0], o[1]), M::pack(o[2], o[3])};
-            *reinterpret_cast<u32x2*>(static_cast<char*>(a.out) + (out_row * D + 16 * mt + 4 * g4) * 2) = packed;
-          }
-        } else {
-          const int64_t ws = out_row * nsplit + split;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            *reinterpret_cast<f32x4*>(&ws_acc[ws * D + 16 * mt + 4 * g4]) = acc[t][mt];
-          if (g4 == 0) {
-            ws_max[ws] = m[t];
-            ws_sum[ws] = lsum;
-          }
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<f32x4*>(&ws_acc[ws * D + 16 * mt + 4 * g4]) = acc[t][mt];
+        if (g4 == 0) {
+          ws_max[ws] = m[t];
+          ws_sum[ws] = lsum;
         }
       }
-    }();
-    __syncthreads();  // every wave is done with this unit's LDS before the next one's DMA
+    }
+  };
+  if constexpr (kPersistentPrefill<D>) {
+    const int g = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
+    for (int round = 0;; ++round) {
+      const int unit = round * g + ((round & 1) ? g - 1 - b : b);
+      if (unit >= n_units) break;  // units only grow with the round
+      run_unit(unit);
+      __syncthreads();  // every wave is done with this unit's LDS before the next one's DMA
+    }
+  } else {
+    if (static_cast<int>(blockIdx.x) < n_units) run_unit(static_cast<int>(blockIdx.x));
   }
 }
 
@@ -679,12 +689,12 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
   with_score_map(qk_scale, a.softcap, a.window, [&](auto map) {
     using S = decltype(map);
     if (a.kv_fp8) {
-      const uint64_t grid = std::min<uint64_t>(n, prefill_grid<E, D, S, true>());
+      const uint64_t grid = kPersistentPrefill<D> ? std::min<uint64_t>(n, prefill_grid<E, D, S, true>()) : n;
       hipLaunchKernelGGL((prefill_kernel<E, D, S, true>), dim3(static_cast<uint32_t>(grid)),
                          dim3(prefill_threads(D)), 0, stream, a, group, pos_per_tile, nsplit, plan,
                          plan_count, map, ws_max, ws_sum, ws_acc);
     } else {
-      const uint64_t grid = std::min<uint64_t>(n, prefill_grid<E, D, S, false>());
+      const uint64_t grid = kPersistentPrefill<D> ? std::min<uint64_t>(n, prefill_grid<E, D, S, false>()) : n;
       hipLaunchKernelGGL((prefill_kernel<E, D, S, false>), dim3(static_cast<uint32_t>(grid)),
                          dim3(prefill_threads(D)), 0, stream, a, group, pos_per_tile, nsplit, plan,
                          plan_count, map, ws_max, ws_sum, ws_acc);
