@@ -87,6 +87,27 @@ def test_decode_small(gpu, case, partition_size):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("case", [("fp32", 4, 2, 64), ("bf16", 8, 2, 128), ("fp16", 4, 4, 256)],
+                         ids=["fp32-h4x2-d64", "bf16-h8x2-d128", "fp16-h4x4-d256"])
+def test_decode_more_than_64_partitions(gpu, case):
+    """Contexts of more than 64 partitions (64-token partitions, up to 5,000
+    tokens): the reduce's merge of more partitions than a wave has lanes, beside
+    rows of a few partitions and rows that one work item covers."""
+    dtype, hq, hkv, d_ = case
+    say(f"decode >64 partitions {case}")
+    w = W.small_case(910 + hq + d_, num_seqs=6, ctx_lo=1, ctx_hi=900, num_heads=hq,
+                     num_kv_heads=hkv, head_dim=d_, block_size=16, dtype=dtype,
+                     extra_ctx=[5000, 4097, 4096, 64])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    out = run_decode(w, d, 64)
+    torch.cuda.synchronize()
+    kc, vc = written_caches(w)
+    err = max_err(out, oracle_decode(w, kc, vc))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
 @pytest.mark.parametrize("case", [("bf16", 16, 2, 64), ("fp16", 4, 4, 128), ("bf16", 2, 2, 256)],
                          ids=["bf16-h16x2-d64", "fp16-h4x4-d128", "bf16-h2x2-d256"])
 def test_decode_joined_partitions(gpu, case):
