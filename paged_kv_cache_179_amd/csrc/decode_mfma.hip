@@ -34,7 +34,8 @@
 //
 // The kernel is persistent: as many workgroups as fit on the device, each
 // looping over work units (one (sequence, partition) item of the plan, one KV
-// head, up to 16 of its query heads), statically: units b, b + grid, ...
+// head, up to 16 of its query heads), statically: units b, 2 grid - 1 - b,
+// 2 grid + b, ... of the longest-first plan.
 // Four waves take the unit's 16-token passes in turn and merge through LDS at
 // the end of the unit; the first pass of the next unit is already in flight
 // by then.
@@ -208,6 +209,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   int u = blockIdx.x;
   if (u >= n_units) return;
   const int stride = gridDim.x;
+  // Round r of the persistent loop takes unit r * G + b, or r * G + G - 1 - b
+  // in odd rounds (G workgroups): over the longest-first plan, a workgroup that
+  // drew a short unit in one round draws a long one in the next.
+  int rnd = 0;
+  auto unit_at = [&](int r) {
+    const int b = static_cast<int>(blockIdx.x);
+    return r * stride + ((r & 1) ? stride - 1 - b : b);
+  };
 
   const int group = a.num_heads / a.num_kv_heads;
   const int P = a.part_tokens;
@@ -504,15 +513,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     __syncthreads();
   };
 
-  // Persistent loop over units u, u + grid, u + 2 grid, ... (the plan is
-  // ordered longest first, so every round of the grid takes units of similar
-  // length).  Each wave keeps one DMA in flight ahead of the pass it
+  // Persistent loop over the units of unit_at(0), unit_at(1), ... (the plan
+  // is ordered longest first, so every round of the grid takes units of
+  // similar length).  Each wave keeps one DMA in flight ahead of the pass it
   // computes, and the first pass of the next unit is issued before the
   // current unit's merge, so its latency overlaps the merge.  Wave 0 also
   // stages the next unit's query rows; those NQ DMAs are ordered before a
   // pass's and waited with it.
   Unit cur = info(u);
-  Unit nxt = info(u + stride);
+  Unit nxt = info(unit_at(1));
   int qb = 0;
   if (wave == 0) {
     issue_q(cur, 0);
@@ -578,9 +587,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
       // At most the two slots from csl on are in flight; the one before is free.
       finish(cur, csl == 0 ? NS - 1 : csl - 1);
       if (!nxt.valid) break;
-      u += stride;
+      ++rnd;
       cur = nxt;
-      nxt = info(u + stride);
+      nxt = info(unit_at(rnd + 1));
       qb ^= 1;
       ic = in;
       in = 0;
@@ -636,9 +645,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     // the next query tile has landed.
     finish(cur, slot ^ 1);
     if (!nxt.valid) break;
-    u += stride;
+    ++rnd;
     cur = nxt;
-    nxt = info(u + stride);
+    nxt = info(unit_at(rnd + 1));
     qb ^= 1;
   }
 }
