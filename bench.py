@@ -9,7 +9,8 @@ fp16, contexts U[512, 4096], 512-token partitions); the other four workloads
 are measured the same way and reported under "workloads".
 
 Timing: HIP events on the stream the kernels run on (torch's current stream),
-one pair per kernel, K timed steps after W warm-up steps.  Between steps, and
+one pair per kernel, K timed steps after W warm-up steps (per phase: the mean,
+and the median, p10 and p90 over the steps).  Between steps, and
 outside the events, a 512 MiB fill evicts the L2s and the 256 MB last-level
 cache so that every step reads its K/V from HBM.
 
@@ -213,6 +214,9 @@ def summarize(name, w, wk, t, steps):
          "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
          "block_size": w.block_size, "partition_size": w.partition_size,
          "ms": {k: round(v, 5) for k, v in mean.items()},
+         "ms_median": {k: round(float(np.median(v)), 5) for k, v in t.items() if not k.startswith("_")},
+         "ms_p10": {k: round(float(np.percentile(v, 10)), 5) for k, v in t.items() if not k.startswith("_")},
+         "ms_p90": {k: round(float(np.percentile(v, 90)), 5) for k, v in t.items() if not k.startswith("_")},
          "step_bytes": wk["step_bytes"],
          "step_gbs": wk["step_bytes"] / (mean["step"] * 1e-3) / 1e9}
     if "partitions" in mean:
