@@ -16,9 +16,9 @@
 //   (for MQA, 16 positions x 8 heads).  A wave's rows are 16-row MFMA tiles;
 //   their query rows stay in registers.
 // * Keys go by passes of 32.  Each pass's K and V rows are copied HBM -> LDS by
-//   the gfx950 global-to-LDS DMA, a quarter of the rows by each wave, into one
-//   of three or four buffers: the next passes are in flight while one is
-//   computed.
+//   the gfx950 global-to-LDS DMA, a quarter of the rows by each of four
+//   waves, into one of three or four buffers: the next passes are in flight
+//   while one is computed.
 //   Rows are stored with their 16-byte chunks rotated (K by the row, V by twice
 //   the row) so that the compute reads below are bank-conflict free.
 // * Scores, transposed: S^T = K Q^T (keys x rows).  Lane l of the accumulator
@@ -204,12 +204,17 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   constexpr int NTW = prefill_row_tiles(D);  // row tiles per wave
   constexpr int WAVES = prefill_threads(D) / 64;
   constexpr int RPW = 16 * NTW;              // rows per wave
-  constexpr int WKEYS = kKeyTile / WAVES;    // keys each wave copies per pass
+  // Waves that issue the DMA: with eight waves (two per SIMD) only the first
+  // four, each for twice the keys, so that on every SIMD one wave computes
+  // while the other stalls in the DMA issue (1-2% on the Gemma chunks; all
+  // eight issuing, or two, were slower).
+  constexpr int DW = WAVES == 8 ? 4 : WAVES;
+  constexpr int WKEYS = kKeyTile / DW;       // keys each of them copies per pass
   static_assert(KV8 || WKEYS % RPI == 0, "a wave copies whole DMA instructions");
   // Cached rows: 2 D bytes (16-bit) or D bytes (E4M3, converted in LDS into
   // the 16-bit tile the MFMAs read).
   constexpr int CNC = KV8 ? NC / 2 : NC;                 // 16-byte chunks per cached row
-  constexpr int NDK = (WKEYS * CNC + 63) / 64;          // DMA instructions per wave per pass, K or V
+  constexpr int NDK = (WKEYS * CNC + 63) / 64;          // DMA instructions per issuing wave per pass, K or V
   constexpr int NDW = 2 * NDK;                          // ... K and V
   constexpr int KB = D / 32;            // k-steps of the score product
   constexpr int MT = D / 16;            // 16-dim output tiles
@@ -290,7 +295,7 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
     // the pass loop takes it with a lane read instead of a memory round trip.
     static_assert(kSplitKeys / kKeyTile <= 64, "one lane per pass");
     int blk_lane = 0;
-    if ((1 << lbs) >= WKEYS && lane * kKeyTile < key_hi - key_lo) {
+    if ((1 << lbs) >= WKEYS && wave < DW && lane * kKeyTile < key_hi - key_lo) {
       blk_lane = a.block_tables[trow + (min(key_lo + lane * kKeyTile + wave * WKEYS, key_hi - 1) >> lbs)];
       blk_lane = (blk_lane < 0 || blk_lane >= a.num_blocks) ? 0 : blk_lane;
     }
@@ -332,9 +337,11 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
     auto rot_k = [](int r) { return r % NC; };
     auto rot_v = [](int r) { return D == 64 ? (r & ~1) % NC : (2 * r) % NC; };
 
-    // This wave's share of pass `p`'s DMA (keys 8 wave .. 8 wave + 7 of the
-    // pass) into buffer `b`.  Keys past the range are clamped to its last key.
+    // This wave's share of pass `p`'s DMA (keys WKEYS wave .. WKEYS (wave + 1)
+    // - 1 of the pass; none for waves past DW) into buffer `b`.  Keys past the
+    // range are clamped to its last key.
     auto issue = [&](int p, int b) {
+      if (wave >= DW) return;
       const int k0 = key_lo + p * kKeyTile + wave * WKEYS;
       const char* kd = reinterpret_cast<const char*>(&s_kv[b][0][wave * WKEYS][0]);
       const char* vd = reinterpret_cast<const char*>(&s_kv[b][1][wave * WKEYS][0]);
