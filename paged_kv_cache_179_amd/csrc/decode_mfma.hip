@@ -9,9 +9,14 @@
 //
 // * A pass is one 16-token tile.  Its K and V rows are copied HBM -> LDS by the
 //   gfx950 global-to-LDS DMA, as in the vector kernel: two slots per wave,
-//   with the next pass in flight while this one is computed.  The block id of
-//   a pass comes through a scalar load, so the only vector-memory operations
-//   in flight are the DMAs that the explicit waits count.
+//   with the next pass in flight while this one is computed (three slots and
+//   two passes in flight for E4M3 caches, whose passes are half the bytes).
+//   The block id of a pass comes through a scalar load, so the only
+//   vector-memory operations in flight are the DMAs that the explicit waits
+//   count.
+// * E4M3 caches: keys are widened to 16 bits in registers, right before the
+//   score MFMAs; values into a per-wave 16-bit tile in LDS that the
+//   transposing reads below use.
 // * Scores: S^T = K Q^T with v_mfma_f32_16x16x32_{bf16,f16}.  The A operand is
 //   the tile's key rows, one 16-byte LDS read per lane per 32 dims.  The B
 //   operand is the group's query rows, loaded once into registers; up to 16
