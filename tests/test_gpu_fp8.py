@@ -160,3 +160,47 @@ def test_fp8_prefill(gpu, case):
     err = max_err(out, ref)
     say(f"  max abs err {err:.3e}")
     assert err <= TOL[dtype]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["llama2_7b", "qwen25_7b"])
+def test_fp8_full_workload_sampled(gpu, name):
+    """Decode over E4M3 copies of a full workload's pools (the codes made by
+    torch's float8_e4m3fn cast, per-tensor scale 1/64), in the launch
+    configuration the bench times, checked on sampled rows against the oracle
+    over the same codes.  Only the sampled rows' blocks are dequantised."""
+    say(f"fp8 full workload {name}")
+    w = W.make(name)
+    d = to_dev(w, gpu)
+    pa.reshape_and_cache(d["new_key"], d["new_value"], d["key_cache"], d["value_cache"],
+                         d["slot_mapping"])
+    scale = 1.0 / 64
+    kc8 = (d["key_cache"].float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    vc8 = (d["value_cache"].float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    del d["key_cache"], d["value_cache"]
+    out = torch.full_like(d["query_decode"], float("nan"))
+    maxc = int(w.context_lens[w.decode_rows].max())
+    pa.decode(out, d["query_decode"], kc8, vc8, d["bt_decode"], d["cl_decode"], w.scale, maxc,
+              partition_size=w.partition_size, k_scale=scale, v_scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    ctx = w.context_lens[w.decode_rows]
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[int(ctx.argmax()), int(ctx.argmin())],
+                                     rng.choice(len(w.decode_rows), 5, replace=False)]))
+    seqs = w.decode_rows[rows]
+    # A compact pool of the sampled rows' blocks, and their tables renumbered into it.
+    nblk = (w.context_lens[seqs] + w.block_size - 1) // w.block_size
+    used = np.unique(np.concatenate([w.block_tables[s, :n] for s, n in zip(seqs, nblk)]))
+    remap = {int(b): i for i, b in enumerate(used)}
+    tables = np.full((len(seqs), int(nblk.max())), -1, dtype=np.int32)
+    for i, (s, n) in enumerate(zip(seqs, nblk)):
+        tables[i, :n] = [remap[int(b)] for b in w.block_tables[s, :n]]
+    ub = torch.from_numpy(used).to(gpu)
+    kq = oracle.fp8_dequantize(kc8[ub].cpu().numpy(), scale)
+    vq = oracle.fp8_dequantize(vc8[ub].cpu().numpy(), scale)
+    ref = oracle.paged_decode(f64(w.query_decode)[rows], kq, vq, tables, w.context_lens[seqs],
+                              w.scale, w.block_size)
+    err = max_err(out[torch.from_numpy(rows).to(gpu)], ref)
+    say(f"  max abs err {err:.3e} over rows {rows.tolist()}")
+    assert err <= TOL[w.dtype]
