@@ -462,9 +462,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   // or workspace writes.
   auto finish = [&](const Unit& x, int pr) {
     float* part_out = part_row(wave, pr, hl);
+    if (hl < x.nh) {  // the merge reads only the unit's heads
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      *reinterpret_cast<f32x4*>(part_out + 16 * mt + 4 * g4) = acc[mt];
+      for (int mt = 0; mt < MT; ++mt)
+        *reinterpret_cast<f32x4*>(part_out + 16 * mt + 4 * g4) = acc[mt];
+    }
     if (lane < kHeadTile) {
       s_max[wave][hl] = m;
       s_sum[wave][hl] = lacc[0];
