@@ -425,6 +425,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     if (tid == kWave - 1) {
       *a.plan_count = incl;
       a.plan_count[1] = k_use;  // log2 of the span, for the reduce
+      a.plan_count[2] = 0;      // units taken from the partition kernel's queue
       s_span = k_use;
     }
   }

@@ -39,8 +39,9 @@
 //
 // The kernel is persistent: as many workgroups as fit on the device, each
 // looping over work units (one (sequence, partition) item of the plan, one KV
-// head, up to 16 of its query heads), statically: units b, 2 grid - 1 - b,
-// 2 grid + b, ... of the longest-first plan.
+// head, up to 16 of its query heads) of the longest-first plan: statically in
+// alternating order (units b, 2 grid - 1 - b, 2 grid + b, ...), or, in long
+// launches, from the third unit on whichever is next in a device-wide queue.
 // Four waves take the unit's 16-token passes in turn and merge through LDS at
 // the end of the unit; the first pass of the next unit is already in flight
 // by then.
@@ -58,6 +59,9 @@ namespace {
 constexpr int kWaves = kDecodeThreads / kWave;
 constexpr int kTile = 16;       // tokens per pass
 constexpr int kHeadTile = 16;   // query heads per workgroup (MFMA N)
+// Launches of at least this many rounds of the grid take their units from a
+// queue rather than in a fixed order.
+constexpr int kQueueRounds = 8;
 constexpr float kLazyMax = 8.f; // log2 of the largest unnormalised probability
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -190,6 +194,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   __shared__ float s_max[kWaves][kHeadTile];
   __shared__ float s_sum[kWaves][kHeadTile];
   __shared__ int s_part[kWaves];
+  // The workgroup's unit after the next one, from the queue.  Written by
+  // thread 0 before a barrier and read by every wave after it; the next write
+  // comes after the next unit's first barrier, so one copy is enough.
+  __shared__ int s_next;
   static_assert(sizeof(s_kv[0][0]) == (KV8 ? kHeadTile / 2 : kHeadTile) * D * sizeof(float),
                 "partial output fills a slot");
   static_assert(!KV8 || sizeof(s_cv[0]) == kHeadTile / 2 * D * sizeof(float),
@@ -211,16 +219,27 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
 
   const int per = a.num_kv_heads * head_chunks;
   const int n_units = *scalar_ptr<cint*>(a.plan_count) * per;
-  int u = blockIdx.x;
+  const int u = blockIdx.x;
   if (u >= n_units) return;
-  const int stride = gridDim.x;
-  // Round r of the persistent loop takes unit r * G + b, or r * G + G - 1 - b
-  // in odd rounds (G workgroups): over the longest-first plan, a workgroup that
-  // drew a short unit in one round draws a long one in the next.
-  int rnd = 0;
-  auto unit_at = [&](int r) {
-    const int b = static_cast<int>(blockIdx.x);
-    return r * stride + ((r & 1) ? stride - 1 - b : b);
+  // Workgroup b of N takes units b and 2 N - 1 - b first.  In round r it
+  // then takes unit r N + b, or r N + N - 1 - b in odd rounds: over the
+  // longest-first plan, a workgroup that drew a short unit in one round draws
+  // a long one in the next.  Launches of at least kQueueRounds rounds instead
+  // hand out the units from 2 N on in plan order from a counter of units
+  // taken, plan_count[2], which the plan kernel zeroes, so that the
+  // workgroups that run fast take more of the short units at the end.  A
+  // workgroup takes one per unit it starts from its second on and stops at
+  // the first past the end, so every workgroup leaves the loop.  (With few
+  // rounds the atomics, all at about the same time, cost more than the
+  // balance gains.)
+  const int NG = static_cast<int>(gridDim.x);
+  const bool queued = n_units >= kQueueRounds * NG;
+  int32_t* const queue = a.plan_count + 2;
+  int rnd = 1;  // round of nxt
+  auto next_unit = [&]() {
+    if (queued) return __builtin_amdgcn_readfirstlane(s_next);
+    ++rnd;
+    return rnd * NG + ((rnd & 1) ? NG - 1 - u : u);
   };
 
   const int group = a.num_heads / a.num_kv_heads;
@@ -460,7 +479,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   // Merge of the four waves' partial states of unit x (slot `pr` of each
   // wave is free and holds its partial output, or half of it) and the output
   // or workspace writes.
-  auto finish = [&](const Unit& x, int pr) {
+  // take: also take the unit after the next one from the queue (into s_next).
+  auto finish = [&](const Unit& x, int pr, bool take) {
     float* part_out = part_row(wave, pr, hl);
     if (hl < x.nh) {  // the merge reads only the unit's heads
 #pragma unroll
@@ -473,6 +493,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     }
     if (lane == 0) s_part[wave] = pr;
     __syncthreads();
+    // Taken before the merge, so that the atomic's latency hides behind it.
+    int taken = 0;
+    if (take && tid == 0) taken = 2 * NG + atomicAdd(queue, 1);
     const int nparts = max(1, (x.ctx + P - 1) / P);
     const int part = x.tb / P;
     const int part_end = min(part + x.span, nparts);
@@ -517,24 +540,25 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
         }
       }
     }
+    if (take && tid == 0) s_next = taken;
     __syncthreads();
   };
 
-  // Persistent loop over the units of unit_at(0), unit_at(1), ... (the plan
-  // is ordered longest first, so every round of the grid takes units of
-  // similar length).  Each wave keeps one DMA in flight ahead of the pass it
-  // computes, and the first pass of the next unit is issued before the
-  // current unit's merge, so its latency overlaps the merge.  Wave 0 also
-  // stages the next unit's query rows; those NQ DMAs are ordered before a
-  // pass's and waited with it.
+  // Persistent loop over the workgroup's units (the plan being ordered
+  // longest first, each round of the grid takes units of similar length).
+  // Each wave keeps one
+  // DMA in flight ahead of the pass it computes, and the first pass of the
+  // next unit is issued before the current unit's merge, so its latency
+  // overlaps the merge.  Wave 0 also stages the next unit's query rows; those
+  // NQ DMAs are ordered before a pass's and waited with it.
   Unit cur = info(u);
-  Unit nxt = info(unit_at(1));
   int qb = 0;
   if (wave == 0) {
     issue_q(cur, 0);
     wait_vmcnt<0>();
   }
   __syncthreads();
+  Unit nxt = info(2 * NG - 1 - u);
   if constexpr (KV8) {
     // Three slots.  A wave's passes, unit after unit, form one stream: pass i
     // of the stream uses slot i mod 3, and up to two passes are in flight
@@ -592,11 +616,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
       // The next query tile has landed before the merge's barrier.
       if (wave == 0 && nxt.valid) wait_upto(2 * NDMA * (issued - q_after));
       // At most the two slots from csl on are in flight; the one before is free.
-      finish(cur, csl == 0 ? NS - 1 : csl - 1);
+      finish(cur, csl == 0 ? NS - 1 : csl - 1, queued && nxt.valid);
       if (!nxt.valid) break;
-      ++rnd;
       cur = nxt;
-      nxt = info(unit_at(rnd + 1));
+      nxt = info(next_unit());
       qb ^= 1;
       ic = in;
       in = 0;
@@ -650,11 +673,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     }
     // Now only the next unit's first pass (if any) is in flight, in `slot`;
     // the next query tile has landed.
-    finish(cur, slot ^ 1);
+    finish(cur, slot ^ 1, queued && nxt.valid);
     if (!nxt.valid) break;
-    ++rnd;
     cur = nxt;
-    nxt = info(unit_at(rnd + 1));
+    nxt = info(next_unit());
     qb ^= 1;
   }
 }

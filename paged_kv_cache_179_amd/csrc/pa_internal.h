@@ -54,7 +54,8 @@ struct DecodeArgs {
   float* ws_sum;   // [S][Hq][P] softmax denominators
   float* ws_acc;   // [S][Hq][P][D] un-normalised partial outputs
   int4* plan;      // [S * P] work items (seq, first partition, span | single << 8, ctx), longest first
-  int32_t* plan_count;  // [0] valid items in `plan`, [1] log2 of the partitions an item joins
+  int32_t* plan_count;  // [0] valid items in `plan`, [1] log2 of the partitions an item joins,
+                        // [2] units taken from the partition kernel's queue
   int32_t num_seqs;
   int32_t num_heads;
   int32_t num_kv_heads;
