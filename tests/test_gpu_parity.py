@@ -108,6 +108,33 @@ def test_decode_more_than_64_partitions(gpu, case):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_decode_unit_queue(gpu, dtype):
+    """A launch long enough that the partition kernel hands out its work units
+    from the device-wide queue: 256 sequences x 32 KV heads (MHA, head_dim
+    128) is at least 8,192 units, over 8 rounds of the persistent grid, which
+    holds at most 512 workgroups at this head size.  Every output row is
+    compared, so a unit taken twice or never shows."""
+    say(f"decode unit queue {dtype}")
+    w = W.small_case(4242, num_seqs=256, ctx_lo=1, ctx_hi=1100, num_heads=32, num_kv_heads=32,
+                     head_dim=128, block_size=16, dtype=dtype, extra_ctx=[1, 512, 513, 1024])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    kc, vc = written_caches(w)
+    ref = oracle_decode(w, kc, vc)
+    maxc = int(w.context_lens[w.decode_rows].max())
+    ws = torch.empty(pa.decode_workspace_bytes(len(w.decode_rows), 32, 128, maxc, 512),
+                     dtype=torch.uint8, device=gpu)
+    for call in range(2):  # one workspace: the plan restarts the queue on every call
+        out = torch.full_like(d["query_decode"], float("nan"))
+        pa.decode(out, d["query_decode"], d["key_cache"], d["value_cache"], d["bt_decode"],
+                  d["cl_decode"], w.scale, maxc, partition_size=512, workspace=ws)
+        torch.cuda.synchronize()
+        err = max_err(out, ref)
+        say(f"  call {call}: max abs err {err:.3e}")
+        assert err <= TOL[dtype]
+
+
 @pytest.mark.parametrize("case", [("bf16", 16, 2, 64), ("fp16", 4, 4, 128), ("bf16", 2, 2, 256)],
                          ids=["bf16-h16x2-d64", "fp16-h4x4-d128", "bf16-h2x2-d256"])
 def test_decode_joined_partitions(gpu, case):
