@@ -183,7 +183,10 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t he
  *                   second kernel through `workspace`.
  *   workspace       device scratch of >= pa_decode_workspace_bytes(...) bytes
  *                   (may be NULL when that is 0); overwritten, no alignment
- *                   requirement beyond 256 bytes.
+ *                   requirement beyond 256 bytes.  It holds the call's work
+ *                   plan and the counter from which the attention kernel's
+ *                   workgroups take their work, so two calls in flight at once
+ *                   (on different streams) need different workspaces.
  */
 pa_status pa_decode(void* out, const void* query, const void* key_cache,
                     const void* value_cache, const int32_t* block_tables,
