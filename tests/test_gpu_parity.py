@@ -108,27 +108,30 @@ def test_decode_more_than_64_partitions(gpu, case):
     assert err <= TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-def test_decode_unit_queue(gpu, dtype):
+@pytest.mark.parametrize("dtype,cap,win", [("fp16", 0.0, 0), ("bf16", 0.0, 0), ("bf16", 30.0, 700)],
+                         ids=["fp16", "bf16", "bf16-cap30-win700"])
+def test_decode_unit_queue(gpu, dtype, cap, win):
     """A launch long enough that the partition kernel hands out its work units
     from the device-wide queue: 256 sequences x 32 KV heads (MHA, head_dim
     128) is at least 8,192 units, over 8 rounds of the persistent grid, which
     holds at most 512 workgroups at this head size.  Every output row is
-    compared, so a unit taken twice or never shows."""
-    say(f"decode unit queue {dtype}")
+    compared, so a unit taken twice or never shows.  The last case adds a
+    soft-cap and a sliding window (units that start inside a partition)."""
+    say(f"decode unit queue {dtype} cap={cap} win={win}")
     w = W.small_case(4242, num_seqs=256, ctx_lo=1, ctx_hi=1100, num_heads=32, num_kv_heads=32,
                      head_dim=128, block_size=16, dtype=dtype, extra_ctx=[1, 512, 513, 1024])
     d = to_dev(w, gpu)
     run_write(w, d)
     kc, vc = written_caches(w)
-    ref = oracle_decode(w, kc, vc)
+    ref = oracle_decode(w, kc, vc, softcap=cap, window=win)
     maxc = int(w.context_lens[w.decode_rows].max())
     ws = torch.empty(pa.decode_workspace_bytes(len(w.decode_rows), 32, 128, maxc, 512),
                      dtype=torch.uint8, device=gpu)
     for call in range(2):  # one workspace: the plan restarts the queue on every call
         out = torch.full_like(d["query_decode"], float("nan"))
         pa.decode(out, d["query_decode"], d["key_cache"], d["value_cache"], d["bt_decode"],
-                  d["cl_decode"], w.scale, maxc, partition_size=512, workspace=ws)
+                  d["cl_decode"], w.scale, maxc, partition_size=512, workspace=ws,
+                  logit_softcap=cap, sliding_window=win)
         torch.cuda.synchronize()
         err = max_err(out, ref)
         say(f"  call {call}: max abs err {err:.3e}")
@@ -309,7 +312,7 @@ def test_tiny_full(gpu):
     torch.cuda.synchronize()
     kc, vc = written_caches(w)
     assert np.array_equal(raw(d["key_cache"]), raw(kc))
-    ref = oracle_decode(w, kc, vc)
+    ref = oracle_decode(w, kc, vc, softcap=cap, window=win)
     err = max_err(out, ref)
     say(f"tiny max abs err {err:.3e}")
     assert err <= 1e-5
