@@ -32,10 +32,11 @@
 //   only moves when a score passes it by more than 2^8, so probabilities stay
 //   <= 256.
 // * Key and value rows are stored in LDS with their 16-byte chunks rotated
-//   per row.  Keys: chunk c of row t at (c - t) mod NC.  Values: at
-//   (c - 2t) mod NC, or (c - (t & ~1)) mod 8 at head_dim 64.  With these, the
-//   16 lanes of a key read, and the 32 lanes of a transposing value read, hit
-//   distinct banks.
+//   per row: chunk c of row t at (c - 2t) mod NC (keys at head_dim 64:
+//   (c - t) mod 8; values: (c - (t & ~1)) mod 8).  Measured with the LDS
+//   bank-conflict counter, a key operand read then costs what a contiguous
+//   16-byte read does (a shift of t costs twice that), and so does a
+//   transposing value read.
 //
 // The kernel is persistent: as many workgroups as fit on the device, each
 // looping over work units (one (sequence, partition) item of the plan, one KV
@@ -127,7 +128,11 @@ struct TileGeo {
   static constexpr int NDMA = kTile / RPI;   // DMA instructions per pass, K or V
   static constexpr int KB = D / 32;          // q.k MFMAs per pass
   static constexpr int MT = D / 16;          // p.V MFMAs per pass
-  __device__ static inline int rot_k(int t) { return t % NC; }
+  // Key and query rows: chunk c of row t sits at (c - rot_k(t)) mod NC.  A
+  // shift of 2 t, not t: with a shift of t the 16-byte reads of one MFMA
+  // operand (16 rows, one chunk column each) take twice the LDS cycles of a
+  // contiguous read, with 2 t (and for the value rows' 2 t) they take the same.
+  __device__ static inline int rot_k(int t) { return D == 64 ? t % NC : (2 * t) % NC; }
   __device__ static inline int rot_v(int t) { return D == 64 ? (t & ~1) % NC : (2 * t) % NC; }
 };
 
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   };
 
   // Per-lane LDS offsets of the compute reads (bytes within one tile).  Key
-  // and query rows share the rotation (chunk c of row t at (c - t) mod NC).
+  // and query rows share the rotation (chunk c of row t at (c - rot_k(t)) mod NC).
   int koff[KB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) koff[kb] = hl * RB + ((4 * kb + g4 - G::rot_k(hl) + NC) % NC) * 16;

@@ -334,7 +334,9 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
     };
 
     // Rotation (in chunks) of key row r and value row r of a tile.
-    auto rot_k = [](int r) { return r % NC; };
+    // A shift of 2 r rather than r: the 16-row operand reads then take the
+    // LDS cycles of a contiguous read instead of twice as many.
+    auto rot_k = [](int r) { return D == 64 ? r % NC : (2 * r) % NC; };
     auto rot_v = [](int r) { return D == 64 ? (r & ~1) % NC : (2 * r) % NC; };
 
     // This wave's share of pass `p`'s DMA (keys WKEYS wave .. WKEYS (wave + 1)
