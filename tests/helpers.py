@@ -41,6 +41,28 @@ def oracle_decode(w, kc, vc, rows=None, softcap=0.0, window=0):
                                window=window)
 
 
+def oracle_decode_per_seq(w, kc, vc, rows=None, softcap=0.0, window=0, to_f64=None):
+    """Oracle decode output for the decode rows (all, or the given subset), fed
+    one sequence at a time with only that sequence's blocks, so that no whole
+    pool is ever widened to float64.  ``kc``/``vc`` are host tensors of the
+    cache's storage type; ``to_f64`` widens a stack of blocks (default: an
+    exact cast; an E4M3 cache passes its dequantisation)."""
+    to_f64 = to_f64 or f64
+    idx = np.arange(len(w.decode_rows)) if rows is None else np.asarray(rows)
+    q = f64(w.query_decode)
+    bs = w.block_size
+    out = np.zeros((len(idx), w.num_heads, w.head_dim), dtype=np.float64)
+    for i, r in enumerate(idx):
+        s = int(w.decode_rows[r])
+        C = int(w.context_lens[s])
+        n = (C + bs - 1) // bs
+        blocks = torch.from_numpy(w.block_tables[s, :n].astype(np.int64))
+        kb, vb = to_f64(kc[blocks]), to_f64(vc[blocks])
+        out[i] = oracle.paged_decode(q[r:r + 1], kb, vb, np.arange(max(n, 1))[None], [C], w.scale,
+                                     bs, softcap=softcap, window=window)[0]
+    return out
+
+
 def oracle_prefill(w, kc, vc, softcap=0.0, window=0):
     seqs = w.prefill_rows
     return oracle.paged_prefill_chunk(f64(w.query_prefill), w.query_start_loc, f64(kc), f64(vc),

@@ -12,7 +12,7 @@ import torch
 import oracle
 import paged_kv_cache_179_amd as pa
 from paged_kv_cache_179_amd import workloads as W
-from tests.helpers import TOL, f64, max_err, to_dev
+from tests.helpers import TOL, f64, max_err, oracle_decode_per_seq, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -164,11 +164,12 @@ def test_fp8_prefill(gpu, case):
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", ["llama2_7b", "qwen25_7b"])
-def test_fp8_full_workload_sampled(gpu, name):
+def test_fp8_full_workload_every_row(gpu, name):
     """Decode over E4M3 copies of a full workload's pools (the codes made by
     torch's float8_e4m3fn cast, per-tensor scale 1/64), in the launch
-    configuration the bench times, checked on sampled rows against the oracle
-    over the same codes.  Only the sampled rows' blocks are dequantised."""
+    configuration the bench times; every output row against the oracle over
+    the same codes, fed one sequence at a time with only its blocks
+    dequantised."""
     say(f"fp8 full workload {name}")
     w = W.make(name)
     d = to_dev(w, gpu)
@@ -184,23 +185,10 @@ def test_fp8_full_workload_sampled(gpu, name):
               partition_size=w.partition_size, k_scale=scale, v_scale=scale)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
-    ctx = w.context_lens[w.decode_rows]
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[int(ctx.argmax()), int(ctx.argmin())],
-                                     rng.choice(len(w.decode_rows), 5, replace=False)]))
-    seqs = w.decode_rows[rows]
-    # A compact pool of the sampled rows' blocks, and their tables renumbered into it.
-    nblk = (w.context_lens[seqs] + w.block_size - 1) // w.block_size
-    used = np.unique(np.concatenate([w.block_tables[s, :n] for s, n in zip(seqs, nblk)]))
-    remap = {int(b): i for i, b in enumerate(used)}
-    tables = np.full((len(seqs), int(nblk.max())), -1, dtype=np.int32)
-    for i, (s, n) in enumerate(zip(seqs, nblk)):
-        tables[i, :n] = [remap[int(b)] for b in w.block_tables[s, :n]]
-    ub = torch.from_numpy(used).to(gpu)
-    kq = oracle.fp8_dequantize(kc8[ub].cpu().numpy(), scale)
-    vq = oracle.fp8_dequantize(vc8[ub].cpu().numpy(), scale)
-    ref = oracle.paged_decode(f64(w.query_decode)[rows], kq, vq, tables, w.context_lens[seqs],
-                              w.scale, w.block_size)
-    err = max_err(out[torch.from_numpy(rows).to(gpu)], ref)
-    say(f"  max abs err {err:.3e} over rows {rows.tolist()}")
+    k_host, v_host = kc8.cpu(), vc8.cpu()
+    del kc8, vc8
+    ref = oracle_decode_per_seq(w, k_host, v_host,
+                                to_f64=lambda t: oracle.fp8_dequantize(t.numpy(), scale))
+    err = max_err(out, ref)
+    say(f"  max abs err {err:.3e} over all {len(w.decode_rows)} rows")
     assert err <= TOL[w.dtype]
