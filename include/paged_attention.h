@@ -66,7 +66,8 @@ typedef enum pa_status {
   PA_ERR_BAD_SHAPE = 2,
   PA_ERR_UNSUPPORTED = 3,
   PA_ERR_WORKSPACE_TOO_SMALL = 4,
-  PA_ERR_LAUNCH = 5
+  PA_ERR_LAUNCH = 5,
+  PA_ERR_TOO_LARGE = 6 /* pa_decode_noalloc: the call needs more than its fixed scratch */
 } pa_status;
 
 typedef enum pa_dtype { PA_DTYPE_F32 = 0, PA_DTYPE_F16 = 1, PA_DTYPE_BF16 = 2 } pa_dtype;
@@ -224,6 +225,35 @@ pa_status pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_s
                            int32_t sliding_window, int32_t partition_size,
                            const void* workspace, size_t workspace_bytes, pa_dtype dtype,
                            void* stream);
+
+/*
+ * pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, semantics and results as pa_decode without the workspace: the
+ * work plan and partition states go to a fixed scratch array of
+ * PA_NOALLOC_SCRATCH_BYTES that the library holds in device memory (one per
+ * device it runs on, kept until the process ends).  Nothing is allocated,
+ * freed or memset by this call; the kernels reset every counter they read.
+ *   - A call whose pa_decode_workspace_bytes(num_seqs, num_heads, head_dim,
+ *     min(max_context_len, max_blocks_per_seq * block_size), partition_size)
+ *     exceeds PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_TOO_LARGE with nothing
+ *     enqueued.
+ *   - All calls on one device share that device's scratch, which keeps the
+ *     last call's contents: two calls that can overlap on one device (other
+ *     streams, other host threads) race and give wrong results.  Serialise
+ *     them, or use pa_decode with a workspace per stream.
+ *   - The first call on a device looks up the scratch's device address (no
+ *     allocation, nothing enqueued); a failure there is PA_ERR_LAUNCH.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+pa_status pa_decode_noalloc(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t max_context_len, float scale, float logit_softcap,
+                            int32_t sliding_window, int32_t partition_size, pa_dtype dtype,
+                            void* stream);
 
 /*
  * Workspace bytes pa_prefill_chunk needs for these sizes (0 if none).

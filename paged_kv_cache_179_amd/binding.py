@@ -41,6 +41,9 @@ _SIGNATURES = {
     "pa_decode": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32, _i32, _i32,
                    _i32, _i32, _i32, _f32, _f32, _i32, _i32, _c_ptr, _size, ctypes.c_int, _c_ptr],
                   ctypes.c_int),
+    "pa_decode_noalloc": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32, _i32,
+                           _i32, _i32, _i32, _i32, _f32, _f32, _i32, _i32, ctypes.c_int, _c_ptr],
+                          ctypes.c_int),
     "pa_decode_partitions": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32,
                               _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _i32, _c_ptr, _size,
                               ctypes.c_int, _c_ptr], ctypes.c_int),
@@ -300,6 +303,24 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
     st = getattr(library(), name)(*args, ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
     _check(name, st)
     return ws
+
+
+def decode_noalloc(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                   value_cache: torch.Tensor, block_tables: torch.Tensor,
+                   context_lens: torch.Tensor, scale: float, max_context_len: int,
+                   partition_size: int = 512, logit_softcap: float = 0.0,
+                   sliding_window: int = 0) -> None:
+    """pa_decode without a workspace (pa_decode_noalloc): the library's fixed
+    per-device scratch holds the plan and partition states, so nothing is
+    allocated.  Calls that may overlap on one device race; 16-bit and fp32
+    caches."""
+    ptrs, (nb, hkv, bs, d, s, hq, mbps, dt) = _decode_common(out, query, key_cache, value_cache,
+                                                             block_tables, context_lens)
+    st = library().pa_decode_noalloc(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], mbps, ptrs[5],
+                                     s, hq, hkv, d, bs, nb, int(max_context_len), float(scale),
+                                     float(logit_softcap), int(sliding_window),
+                                     int(partition_size), PA_DTYPE[dt], _stream(out))
+    _check("pa_decode_noalloc", st)
 
 
 def decode_partitions(*args, **kwargs):

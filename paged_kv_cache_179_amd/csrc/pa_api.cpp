@@ -235,11 +235,12 @@ const char* pa_status_str(int status) {
     case PA_ERR_UNSUPPORTED: return "unsupported dtype, head_dim, block_size or alignment";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_TOO_LARGE: return "call needs more than the fixed scratch of pa_decode_noalloc";
     default: return "unknown status";
   }
 }
 
-int pa_version(void) { return 103; }
+int pa_version(void) { return 104; }
 
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* key_cache,
                                void* value_cache, const int64_t* slot_mapping,
@@ -420,6 +421,39 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
                              sliding_window, partition_size, workspace, workspace_bytes, dtype,
                              &a);
   if (st != PA_OK || num_seqs == 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  st = to_status(pa::launch_decode_partitions(a, s));
+  if (st != PA_OK) return st;
+  return to_status(pa::launch_decode_reduce(a, s));
+}
+
+pa_status pa_decode_noalloc(void* out, const void* query, const void* key_cache,
+                            const void* value_cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t max_context_len, float scale, float logit_softcap,
+                            int32_t sliding_window, int32_t partition_size, pa_dtype dtype,
+                            void* stream) {
+  // Host validation first, before any HIP call: the placeholder workspace
+  // address only lets decode_args check the other arguments and the size; it
+  // is never passed on.
+  pa::DecodeArgs a;
+  void* const placeholder = reinterpret_cast<void*>(uintptr_t(256));
+  pa_status st = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                             context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, max_context_len, scale, logit_softcap,
+                             sliding_window, partition_size, placeholder,
+                             pa::kNoAllocScratchBytes, dtype, &a);
+  if (st == PA_ERR_WORKSPACE_TOO_SMALL) return PA_ERR_TOO_LARGE;
+  if (st != PA_OK || num_seqs == 0) return st;
+  void* scratch = nullptr;
+  if (pa::noalloc_scratch(&scratch) != hipSuccess) return PA_ERR_LAUNCH;
+  st = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                   context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                   num_blocks, max_context_len, scale, logit_softcap, sliding_window,
+                   partition_size, scratch, pa::kNoAllocScratchBytes, dtype, &a);
+  if (st != PA_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   st = to_status(pa::launch_decode_partitions(a, s));
   if (st != PA_OK) return st;

@@ -116,6 +116,11 @@ struct PrefillArgs {
   int32_t fused;
 };
 
+// Size of the fixed device scratch that pa_decode_noalloc uses in place of a
+// workspace (decode_scratch.hip), and its address on the current device.
+constexpr size_t kNoAllocScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+hipError_t noalloc_scratch(void** ptr);
+
 hipError_t launch_reshape_and_cache(const CacheWriteArgs& a, hipStream_t stream);
 hipError_t launch_block_copy(const BlockCopyArgs& a, hipStream_t stream);
 // Bytes each workgroup of the streaming-read probe reads (one sink word each).

@@ -54,7 +54,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(6):
+    for s in range(7):
         assert lib.pa_status_str(s) and lib.pa_status_str(s) != b"unknown status"
     assert lib.pa_status_str(99) == b"unknown status"
     assert lib.pa_version() >= 100
@@ -192,6 +192,36 @@ def test_decode_validation(lib, fn):
     assert need > 0
     assert decode(lib, fn, wsb=need - 1) == WS
     assert decode(lib, fn, s=0, out=N, q=N, kc=N, vc=N, bt=N, cl=N) == OK
+
+
+def decode_noalloc(lib, out=P, q=P, kc=P, vc=P, bt=P, mbps=100, cl=P, s=4, hq=8, hkv=2, d=128,
+                   bs=16, nb=64, maxc=1000, scale=0.1, cap=0.0, win=0, part=512, dt=F16):
+    return lib.pa_decode_noalloc(out, q, kc, vc, bt, mbps, cl, s, hq, hkv, d, bs, nb, maxc, scale,
+                                 cap, win, part, dt, N)
+
+
+def test_decode_noalloc_validation(lib):
+    """Every argument check of pa_decode, then the fixed scratch's limit, all
+    before the library touches a device."""
+    TOO_LARGE = 6
+    assert decode_noalloc(lib, hkv=3) == SHAPE
+    assert decode_noalloc(lib, d=80) == UNSUP
+    assert decode_noalloc(lib, part=100) == SHAPE
+    assert decode_noalloc(lib, win=-1) == SHAPE
+    assert decode_noalloc(lib, out=N) == NULLP
+    assert decode_noalloc(lib, cl=N) == NULLP
+    assert decode_noalloc(lib, q=ctypes.c_void_p((1 << 20) + 4)) == UNSUP
+    assert decode_noalloc(lib, s=0, out=N, q=N, kc=N, vc=N, bt=N, cl=N) == OK
+    # 4096 sequences x 64 heads x 16 partitions of (256 + 2) floats: far past 64 MiB
+    big = dict(s=4096, hq=64, hkv=8, d=256, mbps=512, maxc=8192)
+    assert lib.pa_decode_workspace_bytes(4096, 64, 256, 8192, 512) > 64 << 20
+    assert decode_noalloc(lib, **big) == TOO_LARGE
+    assert decode_noalloc(lib, out=N, **big) == NULLP  # pointer checks come first
+    # The limit counts the context the tables can reach, not max_context_len
+    # alone: with 32-block tables the call fits, passes validation and then
+    # fails at the scratch lookup, since this machine has no device.
+    assert lib.pa_decode_workspace_bytes(4096, 64, 256, 512, 512) <= 64 << 20
+    assert decode_noalloc(lib, **dict(big, mbps=32)) == LAUNCH
 
 
 def test_reduce_validation(lib):
