@@ -241,8 +241,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reduce_kernel(DecodeArg
   // Partitions holding the attended tokens (the window's, or all of them).
   const int p0 = WIN ? window_start(a, ctx) / a.part_tokens : 0;
   const int p1 = (ctx - 1) / a.part_tokens + 1;
-  // Rows whose partitions fit one work item were written by the partition kernel.
-  if (p1 - p0 <= (1 << a.plan_count[1])) return;
+  // Rows whose partitions fit one work item were written by the partition
+  // kernel, unless group items computed some of their partitions.
+  if (p1 - p0 <= (1 << a.plan_count[1]) && (WIN || a.plan_count[3] == 0 || a.seq_shared[seq] == 0))
+    return;
   const int64_t base = static_cast<int64_t>(row) * a.num_parts;
   typedef float vecf __attribute__((ext_vector_type(PER)));
   vecf num = {};
@@ -352,21 +354,182 @@ hipError_t launch_partitions_e(const DecodeArgs& a, hipStream_t stream) {
 // partitions wholly before the window get no work at all.  One workgroup; it
 // sits on the critical path of every decode call, so it reads each context
 // length once.
+//
+// Shared partitions (a.share).  Sharing a prompt prefix means that several
+// block tables name the same physical blocks (wLLM case study, ADR-001 on
+// the KV-cache layout).  A partition whose blocks several sequences' tables
+// name alike is then read once for all of them by a group item: the query
+// rows of all its sequences (up to a.share_max_members per item) against the
+// one stream of keys and values.  The search runs level by level from
+// partition 0.  At level p, every sequence whose partitions 0..p-1 were
+// shared, and whose partition p is full and not its last, hashes the
+// partition's first block id into an LDS table; the smallest sequence with
+// that id leads, and every other one whose whole partition (every block id)
+// matches the leader's joins it.  Group items take the first plan positions;
+// a member's own items start after its shared partitions, and the reduce
+// merges its row.  Which sequences share a group item changes no result: the
+// group path computes each query row on its own.
+// Inclusive prefix sum over a wave (all 64 lanes active); *total gets the
+// wave's sum.  Within each row of 16 lanes by DPP row shifts (lanes shifted
+// in from outside the row add 0), then the row totals by lane reads.
+__device__ inline int wave_scan(int x, int* total) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  *total = r0 + r1 + r2 + r3;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = 64;
 constexpr int kSpanTokens = 2048;
 constexpr int kPlanCtxCache = 8192;  // context lengths kept in LDS
+constexpr int kShareHashBits = 12;
+constexpr int kShareHash = 1 << kShareHashBits;  // twice the sequences searched: probes stay short
+static_assert(kShareHash >= 2 * kShareMaxSeqs, "hash table load: the search sizes it to 2 S");
+static_assert(kShareMaxSeqs <= kPlanCtxCache, "searched sequences keep their context in LDS");
 
 template <bool WIN>
 __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
   __shared__ int hist[3][kPlanBuckets];  // per span choice 1, 2, 4
   __shared__ int s_ctx[kPlanCtxCache];
-  __shared__ int s_span;
+  __shared__ int s_tot[3];  // items per span choice
+  // Shared-partition search (see above).
+  __shared__ int h_key[kShareHash], h_lead[kShareHash], h_cnt[kShareHash];
+  __shared__ int h_off[kShareHash], h_fill[kShareHash];
+  __shared__ int s_qs[kShareMaxSeqs];    // leading partitions of a sequence that group items cover
+  __shared__ int s_slot[kShareMaxSeqs];  // the sequence's hash slot at the current level, or -1
+  __shared__ int s_key[kShareMaxSeqs];   // first block id of the partition searched
+  __shared__ int s_key1[kShareMaxSeqs];  // and of the next partition, read ahead
+  __shared__ int s_ngroup, s_nmem, s_more, s_hit;
   const int tid = threadIdx.x;
+  const bool share = !WIN && a.share != 0;
+  const int P = a.part_tokens;
+  const int64_t mbps = a.max_blocks_per_seq;
   if (tid < 3 * kPlanBuckets) hist[tid / kPlanBuckets][tid % kPlanBuckets] = 0;
+  if (tid == 0) {
+    s_ngroup = 0;
+    s_nmem = 0;
+  }
+  for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+    // The context length and, for the search, the first block id: loads
+    // issued together, one round trip.
+    const int cl = a.context_lens[s];
+    const int key = share ? a.block_tables[s * mbps] : 0;
+    // Partition 1's first block id: a table entry whenever the table reaches
+    // past partition 0 (checked against the context below).
+    const int bpp0 = P >> a.log2_block_size;
+    const int key1 = share && mbps > bpp0 ? a.block_tables[s * mbps + bpp0] : -1;
+    const int c = max(0, min(cl, a.ctx_limit));
+    if (s < kPlanCtxCache) s_ctx[s] = c;
+    if (share) {
+      s_qs[s] = 0;
+      s_key[s] = key;
+      s_key1[s] = key1;
+    }
+  }
   __syncthreads();
 
-  const int P = a.part_tokens;
+  if (share) {  // a.num_seqs <= kShareMaxSeqs, block_size <= P (host-checked)
+    const int bpp = P >> a.log2_block_size;  // blocks per partition
+    // Hash slots: the power of two >= twice the sequences (at least 64).
+    int hbits = 6;
+    while ((1 << hbits) < 2 * a.num_seqs) ++hbits;
+    const int hsize = 1 << hbits;
+    for (int p = 0; p + 1 < a.num_parts; ++p) {  // a shared partition is never a sequence's last
+      for (int i = tid; i < hsize; i += kPlanThreads) {
+        h_key[i] = -1;
+        h_lead[i] = 0x7fffffff;
+        h_cnt[i] = 0;
+        h_fill[i] = 0;
+      }
+      if (tid == 0) {
+        s_more = 0;
+        s_hit = 0;
+      }
+      __syncthreads();
+      for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+        int slot = -1;
+        const int key = s_key[s];
+        if (s_qs[s] == p && s_ctx[s] > (p + 1) * P && key >= 0 && key < a.num_blocks) {
+          slot = static_cast<int>((static_cast<uint32_t>(key) * 0x9E3779B1u) >> (32 - hbits));
+          while (true) {  // at most a.num_seqs keys in twice as many slots
+            const int old = atomicCAS(&h_key[slot], -1, key);
+            if (old == -1) break;
+            if (old == key) {
+              s_hit = 1;  // another sequence starts the partition with this block
+              break;
+            }
+            slot = (slot + 1) & (hsize - 1);
+          }
+          atomicMin(&h_lead[slot], s);
+        }
+        s_slot[s] = slot;
+      }
+      __syncthreads();
+      if (s_hit == 0) break;  // no partition begins with another's block: nothing shared
+      for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+        const int slot = s_slot[s];
+        if (slot < 0) continue;
+        const int lead = h_lead[slot];
+        if (lead == s) continue;
+        // Compare the whole partition's block ids, the loads all in flight at
+        // once (16-byte loads when the table rows allow them).
+        const int32_t* mine = a.block_tables + s * mbps + p * bpp;
+        const int32_t* theirs = a.block_tables + lead * mbps + p * bpp;
+        int diff = 0;
+        if (a.share_vec) {
+          for (int i = 0; i < bpp; i += 4) {
+            const int4 x = *reinterpret_cast<const int4*>(mine + i);
+            const int4 y = *reinterpret_cast<const int4*>(theirs + i);
+            diff |= (x.x ^ y.x) | (x.y ^ y.y) | (x.z ^ y.z) | (x.w ^ y.w);
+          }
+        } else {
+          for (int i = 1; i < bpp; ++i) diff |= mine[i] ^ theirs[i];
+        }
+        if (diff == 0) atomicAdd(&h_cnt[slot], 1);
+        else s_slot[s] = -1;  // first block alike, the rest not: read on its own
+      }
+      __syncthreads();
+      for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+        const int slot = s_slot[s];
+        if (slot < 0 || h_lead[slot] != s || h_cnt[slot] == 0) continue;
+        // A group's leader reserves its member run and its items: runs of
+        // up to share_max_members sequences, the last one shorter.
+        const int n = h_cnt[slot] + 1;
+        const int off = atomicAdd(&s_nmem, n);
+        const int nit = (n + a.share_max_members - 1) / a.share_max_members;
+        const int first = atomicAdd(&s_ngroup, nit);
+        h_off[slot] = off;
+        for (int i = 0; i < nit; ++i) {
+          const int cnt = min(a.share_max_members, n - i * a.share_max_members);
+          a.plan[first + i] =
+              make_int4(off + i * a.share_max_members, p, 1 | (1 << 9) | (cnt << 16), (p + 1) * P);
+        }
+      }
+      __syncthreads();
+      for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+        const int slot = s_slot[s];
+        if (slot < 0 || h_cnt[slot] == 0) continue;  // not shared at this level
+        a.members[h_off[slot] + atomicAdd(&h_fill[slot], 1)] = s;
+        s_qs[s] = p + 1;
+        if (s_ctx[s] > (p + 2) * P) {  // the next level's key
+          s_key[s] = p == 0 ? s_key1[s] : a.block_tables[s * mbps + (p + 1) * bpp];
+          s_more = 1;
+        }
+      }
+      __syncthreads();
+      if (s_more == 0) break;
+    }
+    if (s_ngroup > 0)
+      for (int s = tid; s < a.num_seqs; s += kPlanThreads) a.seq_shared[s] = s_qs[s];
+  }
+  const int ngroup = share ? s_ngroup : 0;
+
   // log2 of the widest span considered: at most 4 partitions, kSpanTokens
   // tokens and the partitions there are.
   int max_k = 0;
@@ -378,73 +541,127 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
   auto ctx_of = [&](int s) {
     return s < kPlanCtxCache ? s_ctx[s] : max(0, min(a.context_lens[s], a.ctx_limit));
   };
-  // Tokens of span slot `slot` (2^k partitions, counted from the partition
-  // that holds the first attended token `lo`, which starts at token `base`) of
-  // a sequence; a sequence with an empty context still owns one item, whose
-  // output rows are zeros.
-  auto span_tokens = [&](int c, int lo, int base, int k, int slot) {
-    if (slot == 0 && c == 0) return 1;
-    if constexpr (!WIN) return min(P << k, c - slot * (P << k));
-    const int first = base + slot * (P << k);
-    return min(first + (P << k), c) - max(first, lo);
+  // A sequence's own items: spans of 2^k partitions from `base` (a partition
+  // boundary: the partition holding the window's first token, the first one
+  // after the shared ones, or 0), the attended tokens from `lo` on.  Every
+  // span is full except, without a window, the last one and, with a window,
+  // the first and the last; a sequence with an empty context still owns one
+  // item, whose output rows are zeros.
+  struct Own {
+    int c, base, lo;
   };
-  auto first_part_token = [&](int lo) { return lo > 0 ? lo - lo % P : 0; };
-  for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
-    const int c = max(0, min(a.context_lens[s], a.ctx_limit));
-    if (s < kPlanCtxCache) s_ctx[s] = c;
-    const int lo = WIN ? window_start(a, c) : 0;
-    const int base = WIN ? first_part_token(lo) : 0;
-    for (int k = 0; k <= max_k; ++k)
-      for (int slot = 0;; ++slot) {
-        const int t = span_tokens(c, lo, base, k, slot);
-        if (t <= 0) break;
-        atomicAdd(&hist[k][kPlanBuckets - 1 - ((t - 1) >> shift[k])], 1);
-      }
+  auto own = [&](int s) {
+    Own o;
+    o.c = ctx_of(s);
+    if constexpr (WIN) {
+      o.lo = window_start(a, o.c);
+      o.base = o.lo - o.lo % P;
+    } else {
+      o.base = share ? s_qs[s] * P : 0;
+      o.lo = o.base;
+    }
+    return o;
+  };
+  auto span_tokens = [&](const Own& o, int k, int slot) {
+    if (slot == 0 && o.c == 0) return 1;
+    const int first = o.base + slot * (P << k);
+    return min(first + (P << k), o.c) - max(first, o.lo);
+  };
+  auto bucket = [&](int k, int t) { return kPlanBuckets - 1 - ((t - 1) >> shift[k]); };
+  // A sequence's spans for span choice k: n of them, the first and the last
+  // placed one by one, those between always full.
+  auto n_spans = [&](const Own& o, int k) {
+    return o.c == 0 ? 1 : (o.c - o.base + (P << k) - 1) / (P << k);
+  };
+  const int lane = tid & (kWave - 1);
+  const int nloop = (a.num_seqs + kPlanThreads - 1) / kPlanThreads;  // whole waves in step
+
+  // 1. Item counts of each span choice (wave sums, one atomic per wave).
+  if (tid < 3) s_tot[tid] = 0;
+  __syncthreads();
+  for (int i = 0; i < nloop; ++i) {
+    const int s = i * kPlanThreads + tid;
+    const bool live = s < a.num_seqs;
+    const Own o = own(live ? s : 0);
+    for (int k = 1; k <= max_k; ++k) {
+      int total;
+      wave_scan(live ? n_spans(o, k) : 0, &total);
+      if (lane == 0) atomicAdd(&s_tot[k], total);
+    }
+  }
+  __syncthreads();
+  int k = 0;  // the widest span that keeps plan_min_items items
+  for (int kk = max_k; kk >= 1; --kk)
+    if (s_tot[kk] + ngroup >= a.plan_min_items) {
+      k = kk;
+      break;
+    }
+  const int span = 1 << k;
+  // 2. Histogram of the chosen spans' lengths.  Full spans all fall in the
+  // top bucket (0): those are summed over the wave first.
+  struct Spans {
+    int n, b_first, b_last, top;  // b_last only when n >= 2; top: spans in bucket 0
+  };
+  auto spans = [&](const Own& o) {
+    Spans x;
+    x.n = n_spans(o, k);
+    x.b_first = bucket(k, span_tokens(o, k, 0));
+    x.b_last = x.n >= 2 ? bucket(k, span_tokens(o, k, x.n - 1)) : -1;
+    x.top = (x.b_first == 0) + max(0, x.n - 2) + (x.b_last == 0);
+    return x;
+  };
+  for (int i = 0; i < nloop; ++i) {
+    const int s = i * kPlanThreads + tid;
+    const bool live = s < a.num_seqs;
+    const Spans x = spans(own(live ? s : 0));
+    int total;
+    wave_scan(live ? x.top : 0, &total);
+    if (lane == 0 && total > 0) atomicAdd(&hist[k][0], total);
+    if (live && x.b_first > 0) atomicAdd(&hist[k][x.b_first], 1);
+    if (live && x.b_last > 0) atomicAdd(&hist[k][x.b_last], 1);
   }
   __syncthreads();
   static_assert(kPlanBuckets == kWave, "one bucket per lane of wave 0");
   if (tid < kWave) {
-    // Wave 0, one bucket per lane: item counts per span, then the exclusive
-    // prefix sum of the chosen span's histogram (the bucket offsets).
-    int k_use = 0;
-    for (int k = max_k; k >= 1; --k) {
-      int items = hist[k][tid];
-      for (int off = 1; off < kWave; off <<= 1) items += __shfl_xor(items, off, kWave);
-      if (items >= a.plan_min_items) {
-        k_use = k;
-        break;
-      }
-    }
-    const int c = hist[k_use][tid];
-    int incl = c;
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int v = __shfl_up(incl, off, kWave);
-      if (tid >= off) incl += v;
-    }
-    hist[k_use][tid] = incl - c;
-    if (tid == kWave - 1) {
-      *a.plan_count = incl;
-      a.plan_count[1] = k_use;  // log2 of the span, for the reduce
-      a.plan_count[2] = 0;      // units taken from the partition kernel's queue
-      s_span = k_use;
+    // Wave 0, one bucket per lane: the exclusive prefix sum of the histogram
+    // (the bucket offsets, after the group items).
+    const int c = hist[k][tid];
+    int tot;
+    const int incl = wave_scan(c, &tot);
+    hist[k][tid] = ngroup + incl - c;
+    if (tid == 0) {
+      *a.plan_count = ngroup + tot;
+      a.plan_count[1] = k;  // log2 of the span, for the reduce
+      a.plan_count[2] = 0;  // units taken from the partition kernel's queue
+      a.plan_count[3] = ngroup;
     }
   }
   __syncthreads();
-  const int k = s_span;
-  const int span = 1 << k;
-  for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
-    const int c = ctx_of(s);
-    const int lo = WIN ? window_start(a, c) : 0;
-    const int base = WIN ? first_part_token(lo) : 0;
-    const int p0 = base > 0 ? base / P : 0;
+  // 3. The items, each at its bucket's next position; a wave's top-bucket
+  // items take one run (one atomic), each lane its part by a prefix sum.
+  const int64_t cap = static_cast<int64_t>(a.num_seqs) * a.num_parts;  // plan entries
+  for (int i = 0; i < nloop; ++i) {
+    const int s = i * kPlanThreads + tid;
+    const bool live = s < a.num_seqs;
+    const Own o = own(live ? s : 0);
+    const Spans x = spans(o);
+    int total;
+    const int top = live ? x.top : 0;
+    const int incl = wave_scan(top, &total);
+    int run = 0;
+    if (lane == 0 && total > 0) run = atomicAdd(&hist[k][0], total);
+    run = __builtin_amdgcn_readlane(run, 0);
+    if (!live) continue;
+    int top_pos = run + incl - top;
+    const int p0 = o.base / P;
     // One item covers the sequence: its output is final, and the reduce skips the row.
-    const int single = c <= base + (P << k) ? 1 : 0;
-    for (int slot = 0;; ++slot) {
-      const int t = span_tokens(c, lo, base, k, slot);
-      if (t <= 0) break;
-      const int pos = atomicAdd(&hist[k][kPlanBuckets - 1 - ((t - 1) >> shift[k])], 1);
-      a.plan[pos] = make_int4(s, p0 + slot * span, span | (single << 8), c);
-    }
+    const int single = (o.base == 0 || WIN) && o.c <= o.base + (P << k) ? 1 : 0;
+    auto put = [&](int slot, int pos) {
+      if (pos >= 0 && pos < cap) a.plan[pos] = make_int4(s, p0 + slot * span, span | (single << 8), o.c);
+    };
+    put(0, x.b_first == 0 ? top_pos++ : atomicAdd(&hist[k][x.b_first], 1));
+    for (int slot = 1; slot < x.n - 1; ++slot) put(slot, top_pos++);
+    if (x.n >= 2) put(x.n - 1, x.b_last == 0 ? top_pos++ : atomicAdd(&hist[k][x.b_last], 1));
   }
 }
 
@@ -484,7 +701,13 @@ DecodeWorkspace decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int
   }
   w.off_count = off;
   w.off_plan = off + 256;
-  w.bytes = w.off_plan + align256(static_cast<size_t>(num_seqs) * std::max(num_parts, 1) * sizeof(int4));
+  const size_t items = static_cast<size_t>(num_seqs) * std::max(num_parts, 1);
+  w.bytes = w.off_plan + align256(items * sizeof(int4));
+  if (num_parts > 1) {
+    w.off_shared = w.bytes;
+    w.off_members = w.off_shared + align256(static_cast<size_t>(num_seqs) * sizeof(int32_t));
+    w.bytes = w.off_members + align256(items * sizeof(int32_t));
+  }
   return w;
 }
 
@@ -493,11 +716,23 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
   DecodeArgs a = args;
   const bool mfma = a.dtype != PA_DTYPE_F32;
   a.plan_min_items = 0;
+  a.share = 0;
   if (mfma) {
     // Join partitions while every persistent workgroup still gets two units.
     const int group = a.num_heads / a.num_kv_heads;
     const int per = a.num_kv_heads * ((group + 15) / 16);
     a.plan_min_items = std::max(1, (2 * decode_mfma_grid(a) + per - 1) / per);
+    // Shared partitions: 16-bit caches, whole contexts, one head chunk per
+    // KV head, blocks of 16+ tokens (one scalar table read per pass).
+    a.share = (!a.kv_fp8 && a.window == 0 && group <= 16 && a.num_seqs >= 2 &&
+               a.num_seqs <= kShareMaxSeqs && a.num_parts > 1 && a.log2_block_size >= 4 &&
+               a.seq_shared != nullptr && a.members != nullptr) ? 1 : 0;
+    a.share_max_members = decode_group_rows(a.head_dim) / group;
+    // The search compares a partition's block ids 16 bytes at a time when
+    // every table row's partitions start 16-byte aligned.
+    const int bpp = a.part_tokens >> a.log2_block_size;
+    a.share_vec = (reinterpret_cast<uintptr_t>(a.block_tables) % 16 == 0 && a.max_blocks_per_seq % 4 == 0 &&
+                   bpp % 4 == 0) ? 1 : 0;
   }
   if (a.window > 0)
     hipLaunchKernelGGL(decode_plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, stream, a);
@@ -511,7 +746,8 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {
   if (a.num_parts <= 1) return hipSuccess;
-  if (a.plan_count == nullptr || a.ws_max == nullptr || a.ws_sum == nullptr || a.ws_acc == nullptr)
+  if (a.plan_count == nullptr || a.ws_max == nullptr || a.ws_sum == nullptr || a.ws_acc == nullptr ||
+      a.seq_shared == nullptr)
     return hipErrorInvalidValue;  // the kernel reads the plan's span and the partial states
   switch (a.dtype) {
     case PA_DTYPE_F32: return launch_reduce_e<F32>(a, stream);

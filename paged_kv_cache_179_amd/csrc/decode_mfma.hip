@@ -57,12 +57,21 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = kDecodeThreads / kWave;
+// Waves of one workgroup.  Eight at head_dim 128, so that one workgroup holds
+// a CU and its waves, all of the same age, get the same share of the memory
+// pipeline (two workgroups on one CU do not: the older one's loads issue
+// first, and the younger one streams at about half its rate).  Four at 256,
+// where eight would not fit the LDS, and at 64, where four workgroups share a
+// CU and small launches fill the device in one round.
+template <int D>
+constexpr int waves_for() {
+  return D == 128 ? 8 : 4;
+}
 constexpr int kTile = 16;       // tokens per pass
 constexpr int kHeadTile = 16;   // query heads per workgroup (MFMA N)
 // Launches of at least this many rounds of the grid take their units from a
 // queue rather than in a fixed order.
-constexpr int kQueueRounds = 8;
+constexpr int kQueueRounds = 1;
 constexpr float kLazyMax = 8.f; // log2 of the largest unnormalised probability
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -165,11 +174,15 @@ struct Unit {
   int span;         // partitions joined in the item (its state goes to the first)
   bool single;      // the sequence has one partition: write the output directly
   int mine;         // passes of this wave (passes w, w + 4, ... of the unit)
+  bool group;       // a shared partition for several sequences: nh = their query rows
+  int moff;         // group: the item's run in a.members (seq = its first member)
 };
 
 template <typename E, int D, typename S, bool KV8>
-__global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs a, int32_t head_chunks,
-                                                                     S score) {
+__global__ __launch_bounds__(waves_for<D>() * kWave) void decode_mfma_kernel(DecodeArgs a, int32_t head_chunks,
+                                                                            S score) {
+  constexpr int kWaves = waves_for<D>();
+  constexpr int kThreads = kWaves * kWave;
   using M = Mma<E>;
   using G = TileGeo<D>;
   constexpr int NC = G::NC, RB = G::RB, RPI = G::RPI, KB = G::KB, MT = G::MT;
@@ -226,17 +239,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   const int n_units = *scalar_ptr<cint*>(a.plan_count) * per;
   const int u = blockIdx.x;
   if (u >= n_units) return;
-  // Workgroup b of N takes units b and 2 N - 1 - b first.  In round r it
-  // then takes unit r N + b, or r N + N - 1 - b in odd rounds: over the
-  // longest-first plan, a workgroup that drew a short unit in one round draws
-  // a long one in the next.  Launches of at least kQueueRounds rounds instead
-  // hand out the units from 2 N on in plan order from a counter of units
-  // taken, plan_count[2], which the plan kernel zeroes, so that the
-  // workgroups that run fast take more of the short units at the end.  A
-  // workgroup takes one per unit it starts from its second on and stops at
-  // the first past the end, so every workgroup leaves the loop.  (With few
-  // rounds the atomics, all at about the same time, cost more than the
-  // balance gains.)
+  // Workgroup b of N takes units b and 2 N - 1 - b first.  Launches of more
+  // than one round of the grid then hand out the units from 2 N on in plan
+  // order from a counter of units taken, plan_count[2], which the plan kernel
+  // zeroes, so that the workgroups that run fast take more of the short units
+  // at the end (per-workgroup traces show rates apart by up to 2x, so a fixed
+  // order leaves a long tail).  A workgroup takes one per unit it starts from
+  // its second on and stops at the first past the end, so every workgroup
+  // leaves the loop.  (Without the queue, in round r a workgroup takes unit
+  // r N + b, or r N + N - 1 - b in odd rounds: over the longest-first plan,
+  // one that drew a short unit in one round draws a long one in the next.)
   const int NG = static_cast<int>(gridDim.x);
   const bool queued = n_units >= kQueueRounds * NG;
   int32_t* const queue = a.plan_count + 2;
@@ -256,6 +268,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   const char* qbase = static_cast<const char*>(a.query);
   cint* plan = scalar_ptr<cint*>(a.plan);  // [item][seq, part, run, ctx]
   cint* tables = scalar_ptr<cint*>(a.block_tables);
+  cint* members = scalar_ptr<cint*>(a.members);
 
   auto info = [&](int uu) {
     Unit x;
@@ -267,10 +280,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     x.ctx = plan[4 * static_cast<int64_t>(j) + 3];
     x.span = span_word & 0xff;
     x.single = (span_word >> 8) & 1;
+    x.group = !KV8 && ((span_word >> 9) & 1);
     x.kvh = r / head_chunks;
     const int chunk = r - x.kvh * head_chunks;
     x.h_first = x.kvh * group + chunk * kHeadTile;
     x.nh = min(kHeadTile, group - chunk * kHeadTile);
+    x.moff = 0;
+    if (x.group) {  // one head chunk per KV head; rows = members x group
+      x.moff = x.seq;
+      x.seq = members[x.moff];
+      x.nh = (span_word >> 16) * group;
+    }
     const int pb = plan[4 * static_cast<int64_t>(j) + 1] * P;
     x.lo = window_start(a, x.ctx);
     // Passes start on a 16-token boundary so that each one stays inside one
@@ -506,7 +526,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     const int part_end = min(part + x.span, nparts);
     // Four consecutive dims of one head per thread and step.
     constexpr int D4 = D / 4;
-    for (int idx = tid; idx < x.nh * D4; idx += kDecodeThreads) {
+    for (int idx = tid; idx < x.nh * D4; idx += kThreads) {
       const int h = idx / D4;
       const int d = (idx - h * D4) * 4;
       float mw[kWaves];
@@ -549,6 +569,131 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
     __syncthreads();
   };
 
+  // Group unit (16-bit caches only): one partition that the block tables of
+  // several sequences share, for all their query rows (member m, head j ->
+  // row m * group + j; up to GT row tiles of 16 per wave, so the partition is
+  // read once for up to decode_group_rows(D) rows).  Every wave computes every
+  // pass: wave w still DMAs passes w, w + 4, ... into its own slots, and after
+  // each round of four passes (one barrier) each wave runs its row tiles over
+  // all four.  Query rows come straight from global memory into registers.
+  // A row's running max moves only on its own scores (the rescale factor is
+  // 1 for the other rows of the tile, an exact no-op), so a row's result does
+  // not depend on which rows share its tile.  Each wave writes its rows'
+  // partition states itself: no merge across waves.
+  //   On entry this wave's pass 0 is in flight in `slot`; on exit the next
+  // unit's first pass is in flight in `slot` and, for a regular next unit,
+  // its query tile has landed in s_q[qb ^ 1] (as after a regular unit).
+  constexpr int GT = decode_group_rows(D) / (kWaves * kHeadTile);  // row tiles per wave
+  static_assert(GT >= 1, "group rows");
+  auto group_unit = [&](const Unit& x, const Unit& nx, int& slot, int qb, bool take) {
+    if constexpr (!KV8) {
+      const int rows = x.nh;
+      const int ntile = (rows + kHeadTile - 1) / kHeadTile;
+      u32x4 qr[GT][KB];
+      f32x4 gacc[GT][MT];
+      f32x4 glacc[GT];
+      float gm[GT];
+      int64_t grow[GT];  // this lane's row: sequence * num_heads + head, or -1
+#pragma unroll
+      for (int i = 0; i < GT; ++i) {
+        const int r = (wave + kWaves * i) * kHeadTile + hl;
+        grow[i] = -1;
+        if (r < rows) {
+          const int mem = r / group;
+          const int sq = a.members[x.moff + mem];
+          grow[i] = static_cast<int64_t>(sq) * a.num_heads + x.kvh * group + (r - mem * group);
+        }
+        const char* qsrc = qbase + (grow[i] < 0 ? 0 : grow[i]) * RB;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          qr[i][kb] = grow[i] < 0 ? u32x4{0u, 0u, 0u, 0u} : load16(qsrc + (4 * kb + g4) * 16);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) gacc[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        glacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        gm[i] = -__builtin_inff();
+      }
+      // One pass (16 keys and values in a slot) for this wave's row tiles.
+      auto gpass = [&](const char* kt) {
+        const char* vt = kt + kTile * RB;
+        u32x4 ka[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) ka[kb] = *reinterpret_cast<const u32x4*>(kt + koff[kb]);
+        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+        s16x4 vv[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) vv[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff[mt]));
+#pragma unroll
+        for (int i = 0; i < GT; ++i) {
+          if (wave + kWaves * i >= ntile) continue;  // wave-uniform
+          f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) sacc = M::qk(ka[kb], qr[i][kb], sacc);
+          float sc[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[e] = score(sacc[e]);
+          const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+          const bool up = mx > gm[i] + kLazyMax;  // this row's own decision
+          if (__builtin_amdgcn_ballot_w64(up) != 0) {  // wave-uniform
+            const float alpha = up ? exp2_fast(gm[i] - mx) : 1.f;  // 0 on the first update
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) gacc[i][mt] *= alpha;
+            glacc[i] *= alpha;
+            gm[i] = up ? mx : gm[i];
+          }
+          const u32x2 pb = {M::pack(exp2_fast(sc[0] - gm[i]), exp2_fast(sc[1] - gm[i])),
+                            M::pack(exp2_fast(sc[2] - gm[i]), exp2_fast(sc[3] - gm[i]))};
+          glacc[i] = M::pv(ones, pb, glacc[i]);
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) gacc[i][mt] = M::pv(__builtin_bit_cast(u32x2, vv[mt]), pb, gacc[i][mt]);
+        }
+      };
+      const int npass = (x.te - x.tb) / kTile;  // full partition
+      const int nround = (npass + kWaves - 1) / kWaves;  // the last one may be short
+      // Where this wave's pass 0 lands (read after round 0's barrier; a wave
+      // with no pass in a round still keeps its slot parity in step).
+      if (lane == 0) s_part[wave] = slot;
+      int gs[kWaves];
+      for (int r = 0; r < nround; ++r) {
+        wait_vmcnt<0>();  // this wave's pass of round r (and at r = 0 its query rows)
+        __syncthreads();  // every wave's pass of round r; every wave done with round r - 1
+        if (r == 0) {
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) gs[w] = __builtin_amdgcn_readfirstlane(s_part[w]);
+        }
+        if (r + 1 < nround) {
+          if ((r + 1) * kWaves + wave < npass) issue(x, r + 1, slot ^ 1);
+        } else {
+          if (wave == 0 && nx.valid && !nx.group) issue_q(nx, qb ^ 1);  // before nx's pass 0
+          if (nx.valid && nx.mine > 0) issue(nx, 0, slot ^ 1);
+        }
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          if (r * kWaves + w < npass) gpass(reinterpret_cast<const char*>(&s_kv[w][(gs[w] + r) & 1][0][0][0]));
+        slot ^= 1;
+      }
+      // The next regular unit's query tile has landed before the barrier below.
+      if (wave == 0 && nx.valid && !nx.group) {
+        if (nx.mine > 0) wait_vmcnt<2 * NDMA>();
+        else wait_vmcnt<0>();
+      }
+      const int part = x.tb / P;
+#pragma unroll
+      for (int i = 0; i < GT; ++i) {
+        if (wave + kWaves * i >= ntile || grow[i] < 0) continue;
+        const int64_t ws = grow[i] * a.num_parts + part;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          *reinterpret_cast<f32x4*>(a.ws_acc + ws * D + 16 * mt + 4 * g4) = gacc[i][mt];
+        if (g4 == 0) {
+          a.ws_max[ws] = gm[i];
+          a.ws_sum[ws] = glacc[i][0];
+        }
+      }
+      if (take && tid == 0) s_next = 2 * NG + atomicAdd(queue, 1);
+      __syncthreads();  // slots free for the next unit; s_next published
+    }
+  };
+
   // Persistent loop over the workgroup's units (the plan being ordered
   // longest first, each round of the grid takes units of similar length).
   // Each wave keeps one
@@ -558,7 +703,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   // NQ DMAs are ordered before a pass's and waited with it.
   Unit cur = info(u);
   int qb = 0;
-  if (wave == 0) {
+  if (wave == 0 && !cur.group) {
     issue_q(cur, 0);
     wait_vmcnt<0>();
   }
@@ -634,11 +779,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_mfma_kernel(DecodeArgs 
   int slot = 0;
   if (cur.mine > 0) issue(cur, 0, slot);
   while (true) {
+    if (cur.group) {
+      group_unit(cur, nxt, slot, qb, queued && nxt.valid);
+      if (!nxt.valid) break;
+      cur = nxt;
+      nxt = info(next_unit());
+      qb ^= 1;
+      continue;
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     lacc = f32x4{0.f, 0.f, 0.f, 0.f};
     m = -__builtin_inff();
-    bool q_todo = wave == 0 && nxt.valid;
+    bool q_todo = wave == 0 && nxt.valid && !nxt.group;
     const bool next_first = nxt.valid && nxt.mine > 0;
     for (int k = 0; k < cur.mine; ++k) {
       if (k + 1 < cur.mine) {
@@ -696,8 +849,8 @@ int persistent_grid() {
   if (g > 0) return g;
   int ncu = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D, S, KV8>, kDecodeThreads,
-                                                    0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D, S, KV8>,
+                                                    waves_for<D>() * kWave, 0) != hipSuccess)
     per_cu = 1;
   g = std::max(1, ncu) * std::max(1, per_cu);
   cache[dev].store(g, std::memory_order_relaxed);
@@ -733,7 +886,7 @@ hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
     using S = decltype(map);
     const uint64_t grid = std::min<uint64_t>(n, static_cast<uint64_t>(persistent_grid<E, D, S, KV8>()));
     hipLaunchKernelGGL((decode_mfma_kernel<E, D, S, KV8>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(kDecodeThreads), 0, stream, a, chunks, map);
+                       dim3(waves_for<D>() * kWave), 0, stream, a, chunks, map);
     return 0;
   });
   return hipGetLastError();

@@ -116,6 +116,8 @@ pa_status decode_args(void* out, const void* query, const void* key_cache, const
   a->ws_acc = g.num_parts > 1 ? reinterpret_cast<float*>(ws + w.off_acc) : nullptr;
   a->plan = reinterpret_cast<int4*>(ws + w.off_plan);
   a->plan_count = reinterpret_cast<int32_t*>(ws + w.off_count);
+  a->seq_shared = g.num_parts > 1 ? reinterpret_cast<int32_t*>(ws + w.off_shared) : nullptr;
+  a->members = g.num_parts > 1 ? reinterpret_cast<int32_t*>(ws + w.off_members) : nullptr;
   a->num_seqs = num_seqs;
   a->num_heads = num_heads;
   a->num_kv_heads = num_kv_heads;
@@ -396,6 +398,7 @@ pa_status pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_s
   a.ws_acc = reinterpret_cast<float*>(const_cast<char*>(ws) + w.off_acc);
   // The partition call's plan: the reduce reads how many partitions an item joined.
   a.plan_count = reinterpret_cast<int32_t*>(const_cast<char*>(ws) + w.off_count);
+  a.seq_shared = reinterpret_cast<int32_t*>(const_cast<char*>(ws) + w.off_shared);
   a.num_seqs = num_seqs;
   a.num_heads = num_heads;
   a.head_dim = head_dim;

@@ -13,6 +13,12 @@ namespace pa {
 constexpr int kDecodeThreads = 256;  // 4 waves per decode workgroup
 constexpr int kSegTokens = 512;      // tokens whose block ids are staged in LDS at once
 constexpr int kMaxHeadsPerWg = 8;    // query heads of one KV head handled by one workgroup
+constexpr int kShareMaxSeqs = 2048;  // decode calls of at most this many sequences look for shared partitions
+// Query rows of one group work unit of the MFMA decode kernel (all the
+// sequences of a shared partition, times the group's query heads): one
+// 16-row tile per wave of its workgroup (eight waves at head_dim 128, four at
+// 64 and 256).
+constexpr int decode_group_rows(int head_dim) { return head_dim == 128 ? 128 : 64; }
 
 struct CacheWriteArgs {
   const void* key;
@@ -53,9 +59,13 @@ struct DecodeArgs {
   float* ws_max;   // [S][Hq][P] running max (log2 units)
   float* ws_sum;   // [S][Hq][P] softmax denominators
   float* ws_acc;   // [S][Hq][P][D] un-normalised partial outputs
-  int4* plan;      // [S * P] work items (seq, first partition, span | single << 8, ctx), longest first
+  int4* plan;      // [S * P] work items, group items first, then the others longest first:
+                   //   (seq, first partition, span | single << 8, ctx), or for a group item
+                   //   (offset in members, partition p, 1 | 1 << 9 | member count << 16, (p + 1) * P)
   int32_t* plan_count;  // [0] valid items in `plan`, [1] log2 of the partitions an item joins,
-                        // [2] units taken from the partition kernel's queue
+                        // [2] units taken from the partition kernel's queue, [3] group items
+  int32_t* seq_shared;  // [S] leading partitions of each sequence that group items compute
+  int32_t* members;     // [S * P] the sequences of each group item, one run per item
   int32_t num_seqs;
   int32_t num_heads;
   int32_t num_kv_heads;
@@ -68,6 +78,9 @@ struct DecodeArgs {
   int32_t num_parts;       // partitions covering ctx_limit
   int32_t plan_min_items;  // the plan may join partitions while it keeps this many items (0: never)
   int32_t window;          // sliding window (tokens attended, ending at the query); 0 = whole context
+  int32_t share;           // look for partitions whose blocks several sequences' tables share
+  int32_t share_max_members;  // sequences one group item may hold (its query rows fit a unit)
+  int32_t share_vec;       // the search may read a partition's block ids 16 bytes at a time
   float scale;
   float softcap;           // logit soft-cap; 0 = none
   pa_dtype dtype;          // query, output (and cache unless kv_fp8)
@@ -79,6 +92,7 @@ struct DecodeWorkspace {
   size_t bytes;
   size_t off_max, off_sum, off_acc;  // partition states (only when P > 1)
   size_t off_count, off_plan;        // work plan (always)
+  size_t off_shared, off_members;    // shared-partition plan (only when P > 1)
 };
 DecodeWorkspace decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                         int32_t num_parts);

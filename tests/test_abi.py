@@ -242,9 +242,11 @@ def test_workspace_sizes(lib):
     assert f(128, 32, 128, 4096, 0) == 256 + a256(128 * 16)       # never split
     assert f(128, 32, 128, 512, 512) == 256 + a256(128 * 16)      # always one partition
     # Eight partitions: max and sum per (seq, head, partition), D floats of
-    # partial output, then the plan with one item per (seq, partition).
+    # partial output, then the plan with one item per (seq, partition), the
+    # shared-partition count per sequence and a group member per (seq, partition).
     n = 128 * 32 * 8
-    expect = 2 * a256(n * 4) + a256(n * 128 * 4) + 256 + a256(128 * 8 * 16)
+    expect = (2 * a256(n * 4) + a256(n * 128 * 4) + 256 + a256(128 * 8 * 16) + a256(128 * 4)
+              + a256(128 * 8 * 4))
     assert f(128, 32, 128, 4096, 512) == expect
     assert f(0, 32, 128, 4096, 512) == 0
     g = lib.pa_prefill_workspace_bytes

@@ -17,7 +17,7 @@ import torch
 import paged_kv_cache_179_amd as pa
 from paged_kv_cache_179_amd import workloads as W
 from tests.helpers import (TOL, f64, max_err, oracle_decode, oracle_decode_per_seq,
-                           oracle_prefill, raw, to_dev, written_caches)
+                           oracle_prefill, raw, read_plan, to_dev, written_caches)
 
 pytestmark = pytest.mark.gpu
 
@@ -136,6 +136,11 @@ def test_decode_unit_queue(gpu, dtype, cap, win):
         err = max_err(out, ref)
         say(f"  call {call}: max abs err {err:.3e}")
         assert err <= TOL[dtype]
+        # The launch did take units from the queue (the counter the plan zeroes).
+        _, count, _, _, _ = read_plan(w, ws, 512)
+        n_units = int(count[0]) * 32
+        say(f"  {n_units} units, {int(count[2])} taken from the queue")
+        assert 0 < count[2] <= n_units
 
 
 @pytest.mark.parametrize("case", [("bf16", 16, 2, 64), ("fp16", 4, 4, 128), ("bf16", 2, 2, 256)],
