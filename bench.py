@@ -22,7 +22,7 @@ Figures:
   roofline       the decode partition kernel alone: its algorithmic bytes / its
                  average event-timed duration, against 8 TB/s;
   cpu_baseline   the fp64 oracle (tests' reference implementation, untuned) on a
-                 bounded sample of the same workload, one host thread;
+                 bounded sample of the same workload, over up to 8 host processes;
   stream_probe   a bare streaming read (the library's probe kernel) and a torch
                  copy on the same box, against the spec, and the partition
                  kernel's rate against the read probe.
@@ -178,6 +178,19 @@ class Step:
         return ph
 
 
+def decode_plan_counts(st):
+    """The decode work plan's counts in the step's workspace after a call
+    (the layout pa_decode_workspace_bytes documents): items, log2 of the
+    partitions an item joins, units taken from the queue, items of shared
+    partitions."""
+    w = st.w
+    P = max(1, -(-min(st.maxc_d, w.max_blocks_per_seq * w.block_size) // w.partition_size))
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    n = len(w.decode_rows) * w.num_heads * P
+    off = 2 * al(n * 4) + al(n * w.head_dim * 4) if P > 1 else 0
+    return [int(x) for x in st.ws_d[off:off + 16].cpu().view(torch.int32).tolist()]
+
+
 def measure(step, steps, warmup, flush_buf):
     """Event-timed phases over `steps` steps (after `warmup`); returns ms lists."""
     phases = step.phases()
@@ -238,51 +251,107 @@ def summarize(name, w, wk, t, steps):
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the oracle on a bounded sample (one host thread).
+# CPU baseline: the oracle on a bounded sample, over the host's cores.
 # ---------------------------------------------------------------------------
-def cpu_baseline(w, budget_s=15.0):
+CPU_WORKERS_MAX = 8  # worker processes (each one thread); the rest of the box's share stays free
+
+
+def _widen(raw, dtype_name):
+    """float64 copy of raw cache bits (exact for every storage type)."""
+    if dtype_name == "bf16":
+        return (raw.astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype_name == "fp16":
+        return raw.view(np.float16).astype(np.float64)
+    return raw.view(np.float32).astype(np.float64)
+
+
+def _cpu_worker(job):
+    """One host process of the CPU baseline: the oracle, one thread, over its
+    share of the sampled sequences (each sequence's blocks widened to float64
+    inside the timed region, as one oracle call would).  Returns seconds."""
+    kpath, vpath, dtype_name, items, scale, bs = job
     from threadpoolctl import threadpool_limits
 
     import oracle
 
-    def f64(t):
-        return t.to(torch.float64).numpy()
+    K = np.load(kpath, mmap_mode="r")
+    V = np.load(vpath, mmap_mode="r")
+    used = 0.0
+    with threadpool_limits(limits=1):
+        for q, b0, nblk, C in items:
+            t0 = time.perf_counter()
+            oracle.paged_decode(q, _widen(np.asarray(K[b0:b0 + nblk]), dtype_name),
+                                _widen(np.asarray(V[b0:b0 + nblk]), dtype_name),
+                                np.arange(nblk)[None], [C], scale, bs)
+            used += time.perf_counter() - t0
+    return used
 
-    # Caches after the step's write, as the oracle computes it (raw bits).
+
+def cpu_baseline(w, max_kv_bytes=6 << 30):
+    """The oracle as it stands (fp64 numpy) on the host: the decode rows of
+    the workload in order, up to max_kv_bytes of attended K/V, spread over
+    worker processes (one thread each) by size; value = sampled bytes / the
+    slowest worker's compute time."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import oracle
+
     raw = {torch.float16: torch.int16, torch.bfloat16: torch.int16, torch.float32: torch.int32}[
         w.key_cache.dtype]
+    # Caches after the step's write, as the oracle computes it (raw bits).
     kc, vc = oracle.reshape_and_cache(w.new_key.view(raw).numpy(), w.new_value.view(raw).numpy(),
                                       w.key_cache.view(raw).numpy(), w.value_cache.view(raw).numpy(),
                                       w.slot_mapping, w.block_size)
-    kc = torch.from_numpy(kc).view(w.key_cache.dtype)
-    vc = torch.from_numpy(vc).view(w.key_cache.dtype)
     eb = w.elem_bytes
     row_kv = w.num_kv_heads * w.head_dim * eb * 2
     qrow = w.num_heads * w.head_dim * eb
-    done_rows = []
-    t_used = 0.0
-    with threadpool_limits(limits=1):
-        for i, s in enumerate(w.decode_rows):
-            C = int(w.context_lens[s])
-            nblk = (C + w.block_size - 1) // w.block_size
-            blocks = torch.from_numpy(w.block_tables[s, :nblk].astype(np.int64))
-            # only the blocks this sequence reads, converted once
-            kb = kc[blocks]
-            vb = vc[blocks]
-            local = np.arange(nblk)
-            q = f64(w.query_decode[i:i + 1])
-            t0 = time.perf_counter()
-            oracle.paged_decode(q, f64(kb), f64(vb), local[None], [C], w.scale, w.block_size)
-            t_used += time.perf_counter() - t0
-            done_rows.append(int(s))
-            if t_used >= budget_s:
-                break
-    toks = int(w.context_lens[done_rows].astype(np.int64).sum())
-    nbytes = toks * row_kv + 2 * len(done_rows) * qrow
-    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "attended_tokens_per_s": toks / t_used, "seconds": round(t_used, 3),
-            "sample": f"oracle decode of the first {len(done_rows)} of {len(w.decode_rows)} "
-                      f"sequences ({toks} attended tokens), fp64 numpy, 1 thread",
+    rows, blocks, items, kv = [], [], [], 0
+    for i, s in enumerate(w.decode_rows):
+        C = int(w.context_lens[s])
+        if rows and kv + C * row_kv > max_kv_bytes:
+            break
+        nblk = (C + w.block_size - 1) // w.block_size
+        q = w.query_decode[i:i + 1].to(torch.float64).numpy()
+        items.append((q, sum(len(b) for b in blocks), nblk, C))
+        blocks.append(w.block_tables[s, :nblk].astype(np.int64))
+        rows.append(int(s))
+        kv += C * row_kv
+    idx = np.concatenate(blocks)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    workers = max(1, min(CPU_WORKERS_MAX, cores, len(items)))
+    shares = [[] for _ in range(workers)]
+    load = [0] * workers
+    for it in sorted(items, key=lambda x: -x[3]):  # longest first onto the least loaded
+        j = int(np.argmin(load))
+        shares[j].append(it)
+        load[j] += it[3]
+    tag = f"/dev/shm/pa_cpu_baseline_{os.getpid()}"
+    paths = (tag + "_k.npy", tag + "_v.npy")
+    try:
+        np.save(paths[0], kc[idx])
+        np.save(paths[1], vc[idx])
+        del kc, vc
+        jobs = [(paths[0], paths[1], w.dtype, sh, w.scale, w.block_size) for sh in shares]
+        with cf.ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+            secs = list(ex.map(_cpu_worker, jobs))
+    finally:
+        for pth in paths:
+            if os.path.exists(pth):
+                os.remove(pth)
+    wall = max(secs)
+    toks = int(w.context_lens[rows].astype(np.int64).sum())
+    nbytes = toks * row_kv + 2 * len(rows) * qrow
+    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "attended_tokens_per_s": toks / wall, "seconds": round(wall, 3),
+            "cpu_seconds": round(sum(secs), 3),
+            "sample": f"oracle decode of the first {len(rows)} of {len(w.decode_rows)} sequences "
+                      f"({toks} attended tokens), fp64 numpy, {workers} processes of one thread "
+                      f"(longest first onto the least loaded); GB/s = sampled bytes / the slowest "
+                      f"process's compute time",
             "cpu": _cpu_model()}
 
 
@@ -662,6 +731,12 @@ def main():
         wk = work(w)
         t = measure(st, args.steps, args.warmup, flush)
         r = summarize(name, w, wk, t, args.steps)
+        if st.has_dec:
+            cnt = decode_plan_counts(st)
+            r["decode_plan"] = {"items": cnt[0], "item_partitions": 1 << cnt[1],
+                                "item_tokens_max": w.partition_size << cnt[1],
+                                "shared_partition_items": cnt[3],
+                                "units": cnt[0] * w.num_kv_heads * -(-(w.num_heads // w.num_kv_heads) // 16)}
         r["wall_ms_per_step_incl_flush"] = t["_wall_s"] / args.steps * 1e3
         results[name] = r
         log(f"{name}: " + json.dumps({k: r[k] for k in r if k.endswith(("gbs", "frac", "_ms", "tflops"))}))
@@ -708,6 +783,8 @@ def main():
                    "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size,
                    "context_lens": "uniform[512,4096]", "partition_size": w.partition_size,
+                   "reduce_kernel": True,
+                   "decode_item_partitions": r.get("decode_plan", {}).get("item_partitions"),
                    "num_blocks": w.num_blocks},
         "hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
         "attended_tokens_per_s": round(r["decode_attended_tokens_per_s"], 1),

@@ -150,11 +150,17 @@ pa_status pa_stream_read_probe(const void* src, int64_t bytes, uint32_t* sink, i
                                void* stream);
 
 /*
- * Workspace bytes pa_decode needs (0 only when num_seqs <= 0): the work plan,
- * 256 + 16 * num_seqs * P bytes with P = ceil(max_context_len /
- * partition_size) (1 when partition_size == 0 or the context fits one
- * partition), and, when P > 1, num_seqs * num_heads * P partial results of
- * (head_dim + 2) floats; each region 256-byte aligned.
+ * Workspace bytes pa_decode needs (0 only when num_seqs <= 0), with
+ * P = ceil(max_context_len / partition_size) (1 when partition_size == 0 or
+ * the context fits one partition).  The regions, in this order, each starting
+ * 256-byte aligned: when P > 1, the partial results (num_seqs * num_heads * P
+ * maxima, as many sums, and as many rows of head_dim floats); then the work
+ * plan: 256 bytes of counts (int32: items, log2 of the partitions an item
+ * joins, units taken from the queue, items of shared partitions) and 16 bytes
+ * per item for num_seqs * P items; when P > 1, num_seqs int32 counts of
+ * shared partitions and num_seqs * P int32 sequence ids of shared-partition
+ * items.  The contents are the library's and change with every call; the
+ * layout is stated for tools that read the plan back.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size);

@@ -62,10 +62,12 @@ namespace {
 // pipeline (two workgroups on one CU do not: the older one's loads issue
 // first, and the younger one streams at about half its rate).  Four at 256,
 // where eight would not fit the LDS, and at 64, where four workgroups share a
-// CU and small launches fill the device in one round.
-template <int D>
+// CU and small launches fill the device in one round; four for E4M3 caches,
+// whose three pipeline slots per wave would leave room for one workgroup of
+// eight (measured slower: llama2-shaped fp8 decode 0.46 against 0.40-0.44 ms).
+template <int D, bool KV8>
 constexpr int waves_for() {
-  return D == 128 ? 8 : 4;
+  return D == 128 && !KV8 ? 8 : 4;
 }
 constexpr int kTile = 16;       // tokens per pass
 constexpr int kHeadTile = 16;   // query heads per workgroup (MFMA N)
@@ -179,9 +181,9 @@ struct Unit {
 };
 
 template <typename E, int D, typename S, bool KV8>
-__global__ __launch_bounds__(waves_for<D>() * kWave) void decode_mfma_kernel(DecodeArgs a, int32_t head_chunks,
+__global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_kernel(DecodeArgs a, int32_t head_chunks,
                                                                             S score) {
-  constexpr int kWaves = waves_for<D>();
+  constexpr int kWaves = waves_for<D, KV8>();
   constexpr int kThreads = kWaves * kWave;
   using M = Mma<E>;
   using G = TileGeo<D>;
@@ -850,7 +852,7 @@ int persistent_grid() {
   int ncu = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 1;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D, S, KV8>,
-                                                    waves_for<D>() * kWave, 0) != hipSuccess)
+                                                    waves_for<D, KV8>() * kWave, 0) != hipSuccess)
     per_cu = 1;
   g = std::max(1, ncu) * std::max(1, per_cu);
   cache[dev].store(g, std::memory_order_relaxed);
@@ -886,7 +888,7 @@ hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
     using S = decltype(map);
     const uint64_t grid = std::min<uint64_t>(n, static_cast<uint64_t>(persistent_grid<E, D, S, KV8>()));
     hipLaunchKernelGGL((decode_mfma_kernel<E, D, S, KV8>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(waves_for<D>() * kWave), 0, stream, a, chunks, map);
+                       dim3(waves_for<D, KV8>() * kWave), 0, stream, a, chunks, map);
     return 0;
   });
   return hipGetLastError();

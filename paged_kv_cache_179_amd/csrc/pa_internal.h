@@ -17,7 +17,7 @@ constexpr int kShareMaxSeqs = 2048;  // decode calls of at most this many sequen
 // Query rows of one group work unit of the MFMA decode kernel (all the
 // sequences of a shared partition, times the group's query heads): one
 // 16-row tile per wave of its workgroup (eight waves at head_dim 128, four at
-// 64 and 256).
+// 64 and 256; group units only arise with 16-bit caches).
 constexpr int decode_group_rows(int head_dim) { return head_dim == 128 ? 128 : 64; }
 
 struct CacheWriteArgs {
