@@ -32,13 +32,14 @@
 //   ones operand sums the rounded probabilities (the softmax denominator).
 // * The keys of a chunk are split in ranges of kSplitKeys so that long contexts
 //   spread over several workgroups; each range writes an (m, l, acc) partial
-//   per row and prefill_merge combines them by log-sum-exp weights, as the
-//   decode reduce does.  Rows whose keys fit one range are written directly.
+//   per row and prefill_merge_kernel combines them by log-sum-exp weights, as
+//   the decode reduce does.  Rows whose keys fit one range are written directly.
 //
 // Scores are kept in log2 units (scale * log2 e folded in): one v_exp_f32 per
 // probability.  The running max is only moved when a score passes it by 2^8.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "lds_dma.h"
@@ -221,7 +222,10 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   // [buffer][K or V][key][chunk]; NBUF - 1 passes in flight ahead of the one
   // computed (at head_dim 256 the 8-wave workgroup has the CU to itself).
   constexpr int NBUF = D == 256 ? 4 : 3;
-  __shared__ u32x4 s_kv[NBUF][2][kKeyTile][CNC];
+  // K tiles and V tiles, each at an address known when the kernel is built:
+  // a pass reads its operands at a lane offset plus a constant.
+  __shared__ u32x4 s_k[NBUF][kKeyTile][CNC];
+  __shared__ u32x4 s_v[NBUF][kKeyTile][CNC];
   __shared__ u32x4 s_cv[KV8 ? 2 : 1][kKeyTile][KV8 ? NC : 1];  // converted pass (E4M3 caches)
 
   // At head_dim 256 (one 8-wave workgroup per CU) the launch is persistent:
@@ -345,8 +349,8 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
     auto issue = [&](int p, int b) {
       if (wave >= DW) return;
       const int k0 = key_lo + p * kKeyTile + wave * WKEYS;
-      const char* kd = reinterpret_cast<const char*>(&s_kv[b][0][wave * WKEYS][0]);
-      const char* vd = reinterpret_cast<const char*>(&s_kv[b][1][wave * WKEYS][0]);
+      const char* kd = reinterpret_cast<const char*>(&s_k[b][wave * WKEYS][0]);
+      const char* vd = reinterpret_cast<const char*>(&s_v[b][wave * WKEYS][0]);
       if constexpr (KV8) {
         // E4M3 rows (D bytes) land unrotated, WKEYS * CNC 16-byte pieces per
         // wave: the conversion applies the rotations.  Lanes past the wave's
@@ -449,11 +453,56 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       m[t] = -__builtin_inff();
     }
 
-    auto compute = [&](int p, int b) {
+    // This lane's operand LDS addresses in buffer 0, for the key rows 0-15 of
+    // a pass (rows 16-31 sit 16 rows further on at the same rotation: both
+    // rotations repeat every 16 rows).  Held in registers for the unit, so
+    // that each operand read in the pass loop is a lane address plus a
+    // constant (buffer, half) in the instruction's offset field.  E4M3 caches
+    // read the converted tile.
+    typedef __attribute__((address_space(3))) const char lds_char;
+    const uint32_t k_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (lds_char*)(KV8 ? static_cast<const void*>(&s_cv[0][0][0]) : static_cast<const void*>(&s_k[0][0][0]))));
+    const uint32_t v_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (lds_char*)(KV8 ? static_cast<const void*>(&s_cv[1][0][0]) : static_cast<const void*>(&s_v[0][0][0]))));
+    uint32_t kop[KB], vop[MT];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kop[kb] = k_lds + koff(0, kb);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) vop[mt] = v_lds + voff(0, mt);
+
+    // One pass out of buffer B (a compile-time constant, so that the buffer's
+    // offset folds into the LDS instructions).  Unless `full` (every row of
+    // the wave sees every key of the pass), each score is checked against its
+    // row's range (the diagonal and window edges).
+    auto compute = [&](int p, auto b_const, bool full) {
+      constexpr int B = decltype(b_const)::value;
+      // The empty asm makes the lane offsets opaque at each pass, so that the
+      // tile's address is added in the LDS instructions' offset field rather
+      // than precomputed for every buffer outside the loop (in registers).
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(kop[kb]));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(vop[mt]));
+      constexpr uint32_t BO = KV8 ? 0 : B * kKeyTile * RB;  // the buffer's offset from buffer 0
+      static_assert(BO + 16 * RB < 65536, "fits the LDS instruction offset");
       const int k0 = key_lo + p * kKeyTile;
-      const char* kt = KV8 ? reinterpret_cast<const char*>(&s_cv[0][0][0])
-                           : reinterpret_cast<const char*>(&s_kv[b][0][0][0]);
-      const char* vt = kt + kKeyTile * RB;
+      typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      auto read_v = [&](int mt) {
+        const u32x2 v0 = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(static_cast<uintptr_t>(vop[mt] + BO))));
+        const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
+                                                       static_cast<uintptr_t>(vop[mt] + BO + 16 * RB))));
+        return u32x4{v0[0], v0[1], v1[0], v1[1]};
+      };
+      // Every key operand of the pass is read before the first product, so
+      // that the reads' latencies overlap instead of adding up.
+      u32x4 ka[2][KB];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          ka[h][kb] = *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(kop[kb] + BO + h * 16 * RB));
       // S^T of the pass: s[h][t] holds keys k0 + 16 h + 4 g4 + i of row 16 t + hl.
       f32x4 s[2][NTW];
 #pragma unroll
@@ -462,13 +511,32 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
         for (int t = 0; t < NTW; ++t) s[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(kt + koff(h, kb));
 #pragma unroll
-          for (int t = 0; t < NTW; ++t) s[h][t] = M::run(ka, q[t][kb], s[h][t]);
+          for (int t = 0; t < NTW; ++t) s[h][t] = M::run(ka[h][kb], q[t][kb], s[h][t]);
         }
       }
-      const bool full = k0 + kKeyTile - 1 <= wave_min_lim && k0 + kKeyTile <= key_hi &&
-                        (!S::kWindow || k0 >= wave_max_lo);  // wave-uniform
+      // The first PV value operands are read during the softmax; each product
+      // then reads the operand PV tiles ahead.
+      constexpr int PV = MT < 8 ? MT : 8;
+      u32x4 va[MT];
+#pragma unroll
+      for (int mt = 0; mt < PV; ++mt) va[mt] = read_v(mt);
+      // An order the scheduler keeps (left to itself it holds one read in
+      // flight at a time, to save registers): the first half's key reads,
+      // then each product of the first half followed by one read of the
+      // second half, then each product of the second half followed by the
+      // first value reads.
+      __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);
+        if (kb < PV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
       u32x4 pb[NTW];
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
@@ -509,20 +577,25 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-        const u32x2 v0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(0, mt))));
-        const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff(1, mt))));
-        const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+        if (mt + PV < MT) va[mt + PV] = read_v(mt + PV);
 #pragma unroll
-        for (int t = 0; t < NTW; ++t) acc[t][mt] = M::run(va, pb[t], acc[t][mt]);
+        for (int t = 0; t < NTW; ++t) acc[t][mt] = M::run(va[mt], pb[t], acc[t][mt]);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        __builtin_amdgcn_sched_group_barrier(0x008, NTW, 1);
+        if (mt + PV < MT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
     };
 
     const int npass = (key_hi - key_lo + kKeyTile - 1) / kKeyTile;
     for (int p = 0; p < NBUF - 1 && p < npass; ++p) issue(p, p);
-    for (int p = 0; p < npass; ++p) {
+    // Pass p uses buffer p % NBUF: the loop runs NBUF passes at a time so that
+    // each one's buffer is a constant.
+    auto step = [&](int p, auto b_const) {
+      constexpr int B = decltype(b_const)::value;
       // Wait for this wave's share of pass p: the passes issued after it may stay in flight.
-      static_assert(NBUF <= 4, "wait cases");
+      static_assert(NBUF == 3 || NBUF == 4, "wait cases and the unrolled pass loop");
       switch (min(NBUF - 2, npass - 1 - p)) {
         case 2: wait_vmcnt<2 * NDW>(); break;
         case 1: wait_vmcnt<NDW>(); break;
@@ -531,19 +604,19 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       // Every wave's share of pass p has landed, and every wave is done with
       // pass p - 1, whose buffer the next DMA reuses.
       __syncthreads();
-      if (p + NBUF - 1 < npass) issue(p + NBUF - 1, (p + NBUF - 1) % NBUF);
+      if (p + NBUF - 1 < npass) issue(p + NBUF - 1, (B + NBUF - 1) % NBUF);
       if constexpr (KV8) {
         // All threads turn the pass's E4M3 K and V rows into the rotated 16-bit
         // tile; the next iteration's barrier keeps it until every wave is
         // done with it.
-        const int b = p % NBUF;
+        const int b = B;
 #pragma unroll
         for (int i = 0; i < 2 * kKeyTile * CNC / (64 * WAVES); ++i) {
           const int idx = static_cast<int>(threadIdx.x) + i * 64 * WAVES;
           const int kv = idx / (kKeyTile * CNC);
           const int t = (idx / CNC) % kKeyTile;
           const int c = 2 * (idx % CNC);
-          const u32x4 w = s_kv[b][kv][t][idx % CNC];
+          const u32x4 w = kv ? s_v[b][t][idx % CNC] : s_k[b][t][idx % CNC];
           const u32x4 lo = {M::template from_fp8<false>(w[0]), M::template from_fp8<true>(w[0]),
                             M::template from_fp8<false>(w[1]), M::template from_fp8<true>(w[1])};
           const u32x4 hi = {M::template from_fp8<false>(w[2]), M::template from_fp8<true>(w[2]),
@@ -555,7 +628,18 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
         __syncthreads();
       }
       const int k0 = key_lo + p * kKeyTile;
-      if (k0 <= wave_last && k0 + kKeyTile > wave_first) compute(p, p % NBUF);  // wave-uniform skip
+      if (k0 <= wave_last && k0 + kKeyTile > wave_first) {  // wave-uniform skip
+        const bool full = k0 + kKeyTile - 1 <= wave_min_lim && k0 + kKeyTile <= key_hi &&
+                          (!S::kWindow || k0 >= wave_max_lo);  // wave-uniform
+        compute(p, b_const, full);
+      }
+    };
+    for (int p0 = 0; p0 < npass; p0 += NBUF) {
+      step(p0, std::integral_constant<int, 0>{});
+      if (p0 + 1 < npass) step(p0 + 1, std::integral_constant<int, 1>{});
+      if (p0 + 2 < npass) step(p0 + 2, std::integral_constant<int, 2 % NBUF>{});
+      if constexpr (NBUF > 3)
+        if (p0 + 3 < npass) step(p0 + 3, std::integral_constant<int, 3 % NBUF>{});
     }
 
 #pragma unroll
@@ -588,6 +672,7 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
         }
       }
     }
+
   };
   if constexpr (kPersistentPrefill<D>) {
     const int g = static_cast<int>(gridDim.x), b = static_cast<int>(blockIdx.x);
@@ -602,31 +687,27 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   }
 }
 
-// One wave per (query token, head): merge the key-range partials of rows
-// whose keys spanned more than one range.
+// One wave per (query token, head): merge the key-range
+// partials of rows whose keys spanned more than one range.  Each wave issues
+// its loads in two rounds (the chunk's bounds, then up to four ranges' states
+// at once), so the kernel costs a few memory latencies.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(PrefillArgs a, int32_t nsplit,
+                                                                int32_t blocks_per_seq,
                                                                 const float* ws_max,
                                                                 const float* ws_sum,
                                                                 const float* ws_acc) {
   constexpr int PER = D / 64;
-  const int64_t rowid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int seq = static_cast<int>(blockIdx.x) / blocks_per_seq;  // each chunk's rows in blocks_per_seq blocks
   const int lane = threadIdx.x & 63;
-  if (rowid >= static_cast<int64_t>(a.num_q_tokens) * a.num_heads) return;
-  const int t = static_cast<int>(rowid / a.num_heads);
-  // Sequence of token t: last s with query_start_loc[s] <= t.
-  int lo = 0, hi = a.num_seqs;  // invariant: qsl[lo] <= t < qsl[hi]
-  if (t < a.query_start_loc[0] || t >= a.query_start_loc[a.num_seqs]) return;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.query_start_loc[mid] <= t) lo = mid; else hi = mid;
-  }
-  const int q_begin = min(max(a.query_start_loc[lo], 0), a.num_q_tokens);
-  const int q_end = min(max(a.query_start_loc[lo + 1], q_begin), a.num_q_tokens);
-  const int ctx = max(0, min(a.context_lens[lo], a.ctx_limit));
+  const int q_begin = min(max(a.query_start_loc[seq], 0), a.num_q_tokens);
+  const int q_end = min(max(a.query_start_loc[seq + 1], q_begin), a.num_q_tokens);
+  const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
   const int qlen = min(q_end - q_begin, ctx);
-  const int pos = t - q_begin;
+  const int r = (static_cast<int>(blockIdx.x) - seq * blocks_per_seq) * 4 + static_cast<int>(threadIdx.x >> 6);  // row of the chunk
+  const int pos = r / a.num_heads;
   if (pos >= qlen) return;
+  const int64_t rowid = static_cast<int64_t>(q_begin + pos) * a.num_heads + (r - pos * a.num_heads);
   const int row_lim = ctx - qlen + pos;
   // Key ranges holding the row's keys (those of its window, or 0 .. row_lim).
   const int p0 = a.window > 0 ? max(0, row_lim - a.window + 1) / kSplitKeys : 0;
@@ -634,23 +715,37 @@ __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(PrefillArgs a, 
   if (p1 - p0 <= 1) return;
   const int64_t base = rowid * nsplit;
 
-  float mx = -__builtin_inff();
-  for (int p = p0 + lane; p < p1; p += 64) mx = fmaxf(mx, ws_max[base + p]);
-  mx = across_groups_max<1>(mx);
-  const float mu = safe_max(mx);
-  float den = 0.f;
-  for (int p = p0 + lane; p < p1; p += 64) den += exp2_fast(ws_max[base + p] - mu) * ws_sum[base + p];
-  den = across_groups_sum<1>(den);
-  float num[PER];
+  // Online merge over groups of four ranges (one group unless the row spans
+  // more than 4096 keys), each group's loads issued together.
+  typedef float vecp __attribute__((ext_vector_type(PER)));
+  vecp num = {};
+  float mrun = -__builtin_inff(), den = 0.f;
+  for (int p = p0; p < p1; p += 4) {
+    vecp v[4];
+    float mp[4], sp[4];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) num[j] = 0.f;
-  for (int p = p0; p < p1; ++p) {
-    const float f = exp2_fast(ws_max[base + p] - mu);
+    for (int u = 0; u < 4; ++u) {
+      const int pu = min(p + u, p1 - 1);
+      v[u] = *reinterpret_cast<const vecp*>(&ws_acc[(base + pu) * D + lane * PER]);
+      mp[u] = p + u < p1 ? ws_max[base + pu] : -__builtin_inff();
+      sp[u] = ws_sum[base + pu];
+    }
+    const float mnew = fmaxf(fmaxf(mrun, fmaxf(mp[0], mp[1])), fmaxf(mp[2], mp[3]));
+    const float mu = safe_max(mnew);
+    const float alpha = exp2_fast(mrun - mu);
+    num *= alpha;
+    den *= alpha;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) num[j] = __builtin_fmaf(f, ws_acc[(base + p) * D + lane * PER + j], num[j]);
+    for (int u = 0; u < 4; ++u) {
+      const float f = exp2_fast(mp[u] - mu);
+      num += f * v[u];
+      den = __builtin_fmaf(f, sp[u], den);
+    }
+    mrun = mnew;
   }
+  const float inv = 1.f / den;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) E::store(a.out, rowid * D + lane * PER + j, num[j] / den);
+  for (int j = 0; j < PER; ++j) E::store(a.out, rowid * D + lane * PER + j, num[j] * inv);
 }
 
 // Workgroups of one persistent prefill launch: as many as fit on the device at once.
@@ -712,10 +807,12 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
   });
   err = hipGetLastError();
   if (err != hipSuccess || nsplit <= 1) return err;
-  const int64_t rows = static_cast<int64_t>(a.num_q_tokens) * a.num_heads;
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_merge_kernel<E, D>), dim3(static_cast<unsigned>((rows + 3) / 4)),
-                     dim3(kThreads), 0, stream, a, nsplit, ws_max, ws_sum, ws_acc);
+  const int64_t blocks_per_seq = (static_cast<int64_t>(a.max_query_len) * a.num_heads + 3) / 4;
+  const int64_t blocks = blocks_per_seq * a.num_seqs;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_merge_kernel<E, D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                     stream, a, nsplit, static_cast<int32_t>(blocks_per_seq), ws_max, ws_sum, ws_acc);
   return hipGetLastError();
 }
 
