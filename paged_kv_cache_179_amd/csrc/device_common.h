@@ -149,6 +149,12 @@ struct ScoreMap {
     }
     return s * mul;
   }
+  // operator()(s) - mu, the exponent of the softmax term of s against a max
+  // mu (one fma without capping).
+  __device__ inline float exponent(float s, float mu) const {
+    if constexpr (CAP) return (*this)(s) - mu;
+    return __builtin_fmaf(s, mul, -mu);
+  }
 };
 template <bool CAP, bool WIN, bool PRECISE = false>
 inline ScoreMap<CAP, WIN, PRECISE> make_score_map(float scale, float softcap) {

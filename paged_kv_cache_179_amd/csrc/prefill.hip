@@ -205,11 +205,11 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   constexpr int NTW = prefill_row_tiles(D);  // row tiles per wave
   constexpr int WAVES = prefill_threads(D) / 64;
   constexpr int RPW = 16 * NTW;              // rows per wave
-  // Waves that issue the DMA: with eight waves (two per SIMD) only the first
-  // four, each for twice the keys, so that on every SIMD one wave computes
-  // while the other stalls in the DMA issue (1-2% on the Gemma chunks; all
-  // eight issuing, or two, were slower).
-  constexpr int DW = WAVES == 8 ? 4 : WAVES;
+  // Waves that issue the DMA: all of them, each for an equal share of the
+  // keys.  (With only the first four of eight issuing, those waves reached
+  // each pass's barrier about a third of a pass after the other four; spread
+  // over all eight, the Gemma chunks' prefill ran 2-3% faster.)
+  constexpr int DW = WAVES;
   constexpr int WKEYS = kKeyTile / DW;       // keys each of them copies per pass
   static_assert(KV8 || WKEYS % RPI == 0, "a wave copies whole DMA instructions");
   // Cached rows: 2 D bytes (16-bit) or D bytes (E4M3, converted in LDS into
@@ -266,6 +266,14 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       row_ok[t] = rpos[t] < npos;
       row_lim[t] = row_ok[t] ? ctx - qlen + pos0 + rpos[t] : -1;
       row_lo[t] = row_lim[t] - win + 1;
+    }
+    // The same bounds as seen from this lane's first key of a pass (4 g4):
+    // lane_lim also stops at the range's end.
+    int lane_lim[NTW], lane_lo[NTW];
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) {
+      lane_lim[t] = min(row_lim[t], key_hi - 1) - 4 * g4;
+      lane_lo[t] = row_lo[t] - 4 * g4;
     }
     // Keys any row of this wave sees (wave-uniform): passes outside are skipped.
     const int wave_last = min(last_key, ctx - qlen + pos0 + min(npos - 1, (wave * RPW + RPW - 1) / group));
@@ -470,41 +478,40 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) vop[mt] = v_lds + voff(0, mt);
 
-    // One pass out of buffer B (a compile-time constant, so that the buffer's
-    // offset folds into the LDS instructions).  Unless `full` (every row of
-    // the wave sees every key of the pass), each score is checked against its
-    // row's range (the diagonal and window edges).
-    auto compute = [&](int p, auto b_const, bool full) {
-      constexpr int B = decltype(b_const)::value;
-      // The empty asm makes the lane offsets opaque at each pass, so that the
-      // tile's address is added in the LDS instructions' offset field rather
-      // than precomputed for every buffer outside the loop (in registers).
+    // A pass out of buffer B (a compile-time constant, so that the buffer's
+    // offset folds into the LDS instructions), in two halves: the scores
+    // S^T = K Q^T (qk), then the online softmax and O^T += V^T P^T (smpv).
+    // Unless `full` (every row of the wave sees every key of the pass), each
+    // score is checked against its row's range (the diagonal and window edges).
+    typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    // The empty asm makes the lane offsets opaque at each use, so that the
+    // tile's address is added in the LDS instructions' offset field rather
+    // than precomputed for every buffer outside the loop (in registers).
+    auto opaque_k = [&]() {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) asm volatile("" : "+v"(kop[kb]));
+    };
+    auto opaque_v = [&]() {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) asm volatile("" : "+v"(vop[mt]));
+    };
+    // s[h][t] holds keys k0 + 16 h + 4 g4 + i of row 16 t + hl.
+    auto qk = [&](auto b_const, f32x4 (&s)[2][NTW]) {
+      constexpr int B = decltype(b_const)::value;
       constexpr uint32_t BO = KV8 ? 0 : B * kKeyTile * RB;  // the buffer's offset from buffer 0
       static_assert(BO + 16 * RB < 65536, "fits the LDS instruction offset");
-      const int k0 = key_lo + p * kKeyTile;
-      typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
-      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-      auto read_v = [&](int mt) {
-        const u32x2 v0 = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(static_cast<uintptr_t>(vop[mt] + BO))));
-        const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
-                                                       static_cast<uintptr_t>(vop[mt] + BO + 16 * RB))));
-        return u32x4{v0[0], v0[1], v1[0], v1[1]};
-      };
-      // Every key operand of the pass is read before the first product, so
-      // that the reads' latencies overlap instead of adding up.
+      opaque_k();
+      // Every key operand of the pass is read before its product, the reads
+      // of the second half during the first half's products, so that their
+      // latencies overlap instead of adding up (an order the scheduler keeps:
+      // left to itself it holds one read in flight at a time, to save registers).
       u32x4 ka[2][KB];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
           ka[h][kb] = *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(kop[kb] + BO + h * 16 * RB));
-      // S^T of the pass: s[h][t] holds keys k0 + 16 h + 4 g4 + i of row 16 t + hl.
-      f32x4 s[2][NTW];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -515,64 +522,76 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
           for (int t = 0; t < NTW; ++t) s[h][t] = M::run(ka[h][kb], q[t][kb], s[h][t]);
         }
       }
-      // The first PV value operands are read during the softmax; each product
-      // then reads the operand PV tiles ahead.
-      constexpr int PV = MT < 8 ? MT : 8;
-      u32x4 va[MT];
-#pragma unroll
-      for (int mt = 0; mt < PV; ++mt) va[mt] = read_v(mt);
-      // An order the scheduler keeps (left to itself it holds one read in
-      // flight at a time, to save registers): the first half's key reads,
-      // then each product of the first half followed by one read of the
-      // second half, then each product of the second half followed by the
-      // first value reads.
       __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, KB * NTW, 0);
+    };
+    auto smpv = [&](int p, auto b_const, bool full, f32x4 (&s)[2][NTW]) {
+      constexpr int B = decltype(b_const)::value;
+      constexpr uint32_t BO = KV8 ? 0 : B * kKeyTile * RB;
+      opaque_v();
+      const int k0 = key_lo + p * kKeyTile;
+      auto read_v = [&](int mt) {
+        const u32x2 v0 = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(static_cast<uintptr_t>(vop[mt] + BO))));
+        const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<lds_s16x4*>(
+                                                       static_cast<uintptr_t>(vop[mt] + BO + 16 * RB))));
+        return u32x4{v0[0], v0[1], v1[0], v1[1]};
+      };
+      // The first PV value operands are read during the softmax (issued
+      // before it); each product then reads the operand PV tiles ahead.
+      constexpr int PV = MT < 8 ? MT : 8;
+      u32x4 va[MT];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);
-        if (kb < PV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
+      for (int mt = 0; mt < PV; ++mt) va[mt] = read_v(mt);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * PV, 0);
       u32x4 pb[NTW];
 #pragma unroll
       for (int t = 0; t < NTW; ++t) {
-        float sc[8];
-        if (full) {
+        // Exponents against the row's current max (an fma each without
+        // capping); masked keys get -inf.  Key k0 + 16 h + 4 g4 + i is in the
+        // row's range when 16 h + i lies in [lo_t - k0, lim_t - k0].
+        const float mu_old = safe_max(m[t]);
+        float e[8];
 #pragma unroll
-          for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[4 * h + i] = score(s[h][t][i]);
-        } else {
+          for (int i = 0; i < 4; ++i) e[4 * h + i] = score.exponent(s[h][t][i], mu_old);
+        if (!full) {
+          const int dhi = lane_lim[t] - k0;
+          const int dlo = lane_lo[t] - k0;
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int key = k0 + 16 * h + 4 * g4 + i;
-              const bool in = (!S::kWindow || key >= row_lo[t]) && key <= row_lim[t] && key < key_hi;
-              sc[4 * h + i] = in ? score(s[h][t][i]) : -__builtin_inff();
+              const bool in = 16 * h + i <= dhi && (!S::kWindow || 16 * h + i >= dlo);
+              e[4 * h + i] = in ? e[4 * h + i] : -__builtin_inff();
             }
         }
-        float mx = sc[0];
+        float mx = e[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sc[i]);
-        mx = max_across_rows(mx);
-        if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyMax) != 0) {  // wave-uniform
-          const float m_new = fmaxf(m[t], mx);
+        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, e[i]);
+        mx = max_across_rows(mx);  // the pass's max, relative to mu_old
+        // Move the max when this pass's passes it by 2^kLazyMax (or is the
+        // row's first finite score); otherwise the exponents stay below it.
+        const bool move = m[t] == -__builtin_inff() ? mx > -__builtin_inff() : mx > kLazyMax;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {  // wave-uniform
+          const float m_new = fmaxf(m[t], mx + mu_old);
           const float alpha = exp2_fast(m[t] - safe_max(m_new));
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) acc[t][mt] *= alpha;
           lacc[t] *= alpha;
+          const float shift = safe_max(m_new) - mu_old;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) e[i] -= shift;
           m[t] = m_new;
         }
-        const float mu = safe_max(m[t]);
-        pb[t] = u32x4{M::pack(exp2_fast(sc[0] - mu), exp2_fast(sc[1] - mu)),
-                      M::pack(exp2_fast(sc[2] - mu), exp2_fast(sc[3] - mu)),
-                      M::pack(exp2_fast(sc[4] - mu), exp2_fast(sc[5] - mu)),
-                      M::pack(exp2_fast(sc[6] - mu), exp2_fast(sc[7] - mu))};
+        pb[t] = u32x4{M::pack(exp2_fast(e[0]), exp2_fast(e[1])), M::pack(exp2_fast(e[2]), exp2_fast(e[3])),
+                      M::pack(exp2_fast(e[4]), exp2_fast(e[5])), M::pack(exp2_fast(e[6]), exp2_fast(e[7]))};
         lacc[t] = M::run(ones, pb[t], lacc[t]);
       }
 #pragma unroll
@@ -588,7 +607,21 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       }
     };
 
+    auto compute = [&](int p, auto b_const, bool full) {
+      f32x4 s[2][NTW];
+      qk(b_const, s);
+      smpv(p, b_const, full, s);
+    };
+
     const int npass = (key_hi - key_lo + kKeyTile - 1) / kKeyTile;
+    auto sees = [&](int p) {  // wave-uniform: some row of this wave sees a key of pass p
+      const int k0 = key_lo + p * kKeyTile;
+      return p < npass && k0 <= wave_last && k0 + kKeyTile > wave_first;
+    };
+    auto full_pass = [&](int p) {  // wave-uniform: every row of this wave sees every key of pass p
+      const int k0 = key_lo + p * kKeyTile;
+      return k0 + kKeyTile - 1 <= wave_min_lim && k0 + kKeyTile <= key_hi && (!S::kWindow || k0 >= wave_max_lo);
+    };
     for (int p = 0; p < NBUF - 1 && p < npass; ++p) issue(p, p);
     // Pass p uses buffer p % NBUF: the loop runs NBUF passes at a time so that
     // each one's buffer is a constant.
@@ -627,12 +660,7 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
         }
         __syncthreads();
       }
-      const int k0 = key_lo + p * kKeyTile;
-      if (k0 <= wave_last && k0 + kKeyTile > wave_first) {  // wave-uniform skip
-        const bool full = k0 + kKeyTile - 1 <= wave_min_lim && k0 + kKeyTile <= key_hi &&
-                          (!S::kWindow || k0 >= wave_max_lo);  // wave-uniform
-        compute(p, b_const, full);
-      }
+      if (sees(p)) compute(p, b_const, full_pass(p));
     };
     for (int p0 = 0; p0 < npass; p0 += NBUF) {
       step(p0, std::integral_constant<int, 0>{});
