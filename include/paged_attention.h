@@ -8,7 +8,7 @@
  *
  *   pa_reshape_and_cache  write the new tokens' K/V into their pool slots
  *                         (mini-vLLM README, "End-to-end throughput vs
- *                         baselines": K/V writes as one indexed assignment);
+ *                         baselines": one scatter for all sequences' K/V);
  *   pa_decode             one query token per sequence attends its whole
  *                         context (wLLM PyPI page, "Features -- Core engine":
  *                         the PagedAttention kernel over a block-based cache),
@@ -304,7 +304,7 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
  * those of pa_reshape_and_cache followed by pa_prefill_chunk.  context_lens
  * still include the chunk.  16-bit caches only.  (wLLM PyPI page, "Features --
  * Core engine": chunked prefill; mini-vLLM README, "End-to-end throughput vs
- * baselines": the K/V write as one indexed assignment.)
+ * baselines": one scatter for all sequences' K/V.)
  */
 pa_status pa_prefill_chunk_fused(void* out, const void* query, const void* key, const void* value,
                                  const int64_t* slot_mapping, const int32_t* query_start_loc,

@@ -8,14 +8,15 @@ shares no code with the HIP library (no kernels, headers, helpers or tables).
 What it computes, and where the pages define it:
 
 * Block pool and tables -- mini-vLLM README, "How it works -- Paged KV-cache":
-  a fixed pool of physical blocks, each holding ``block_size`` token slots,
-  and a per-sequence block table mapping logical positions to physical
-  storage.  Logical token ``t`` of a sequence lives in physical block
-  ``table[t // block_size]`` at offset ``t % block_size``.
+  the cache is a preallocated set of equal blocks of ``block_size`` tokens,
+  and each sequence owns a table that says which physical block holds each
+  of its logical blocks.  Logical token ``t`` of a sequence lives in physical
+  block ``table[t // block_size]`` at offset ``t % block_size``.
 * The cache write -- mini-vLLM README, "End-to-end throughput vs baselines",
-  the paragraph on what changed from the previous run: new K/V are written
-  by one indexed assignment.  Here: one slot per new token,
-  ``slot = block * block_size + offset``; a negative slot is skipped.
+  the paragraph on what changed from the previous run: all new K/V go into
+  the cache in a single scatter rather than sequence by sequence.  Here: one
+  slot per new token, ``slot = block * block_size + offset``; a negative slot
+  is skipped.
 * Attention -- mini-vLLM README, "Attention kernel path": the CPU path is
   standard scaled dot-product attention; wLLM's PyPI page ("CPU inference")
   likewise describes its CPU decode as a plain-PyTorch fallback with the same

@@ -1,8 +1,8 @@
 // Slot-mapped K/V cache write for gfx950.
 //
 // The new tokens' keys and values are scattered into their pool slots in one
-// launch -- the "one indexed assignment per layer instead of a per-sequence
-// loop" of the mini-vLLM README ("End-to-end throughput vs baselines").  Each
+// launch for all sequences, not one sequence at a time (mini-vLLM README,
+// "End-to-end throughput vs baselines").  Each
 // lane moves 16 bytes; the 16-byte chunks of one (token, KV head) row are
 // consecutive lanes, so both the read of key/value and the write into the
 // [block][head][offset][dim] pool are contiguous per row.  Pure bit copy.

@@ -27,6 +27,8 @@
 // Scores are kept in log2 units (scale * log2(e) folded in) so every
 // exponential is one v_exp_f32.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 
 #include "device_common.h"
 #include "decode_common.h"
@@ -711,10 +713,22 @@ DecodeWorkspace decode_workspace_layout(int32_t num_seqs, int32_t num_heads, int
   return w;
 }
 
+// PA_DECODE_KERNEL=vector in the environment (read once): 16-bit caches go
+// through the vector kernel too, the baseline the MFMA kernel is measured
+// against (same results within the 16-bit tolerance; E4M3 caches always take
+// the MFMA kernel).
+static bool vector_kernel_forced() {
+  static const bool forced = [] {
+    const char* e = std::getenv("PA_DECODE_KERNEL");
+    return e != nullptr && std::strcmp(e, "vector") == 0;
+  }();
+  return forced;
+}
+
 hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) {
   if (args.num_seqs <= 0) return hipSuccess;
   DecodeArgs a = args;
-  const bool mfma = a.dtype != PA_DTYPE_F32;
+  const bool mfma = a.dtype != PA_DTYPE_F32 && (a.kv_fp8 || !vector_kernel_forced());
   a.plan_min_items = 0;
   a.share = 0;
   if (mfma) {
@@ -741,7 +755,11 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mfma) return launch_decode_mfma(a, stream);
-  return launch_partitions_e<F32>(a, stream);
+  switch (a.dtype) {
+    case PA_DTYPE_F16: return launch_partitions_e<F16>(a, stream);
+    case PA_DTYPE_BF16: return launch_partitions_e<BF16>(a, stream);
+    default: return launch_partitions_e<F32>(a, stream);
+  }
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a, hipStream_t stream) {

@@ -6,8 +6,8 @@ It holds none of the attention arithmetic, so both the HIP path and the CPU
 oracle can be fed from it without sharing any of the method's code.
 
 The memory model follows the mini-vLLM README ("How it works -- Paged
-KV-cache"): a fixed pool of physical blocks of ``block_size`` token slots and a
-per-sequence table from logical block index to physical block.  Prefix sharing
+KV-cache"): preallocated equal blocks of ``block_size`` tokens, and for each
+sequence a table giving the physical block behind each logical one.  Prefix sharing
 is expressed the way the wLLM case study's ADR-001 ("KV-cache layout") puts it:
 several tables name the same physical blocks.
 
