@@ -117,6 +117,21 @@ __device__ inline float across_groups_sum(float x) {
   return x;
 }
 
+// Inclusive prefix sum over a wave (all 64 lanes active); *total gets the
+// wave's sum.  Within each row of 16 lanes by DPP row shifts (lanes shifted
+// in from outside the row add 0), then the row totals by lane reads.
+__device__ inline int wave_scan(int x, int* total) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47), r3 = __builtin_amdgcn_readlane(x, 63);
+  const int row = (threadIdx.x & (kWave - 1)) >> 4;
+  *total = r0 + r1 + r2 + r3;
+  return x + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Offset used to exponentiate scores against a running max that may still be

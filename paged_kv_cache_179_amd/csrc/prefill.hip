@@ -120,12 +120,13 @@ struct PrefillItem {
   bool valid;
 };
 
-__device__ inline PrefillItem prefill_item(const PrefillArgs& a, int seq, int tile, int split,
-                                           int pos_per_tile) {
+// From the chunk's query_start_loc entries and context length as given.
+__device__ inline PrefillItem prefill_item_at(const PrefillArgs& a, int qsl_begin, int qsl_end, int context_len,
+                                              int tile, int split, int pos_per_tile) {
   PrefillItem it{};
-  it.q_begin = min(max(a.query_start_loc[seq], 0), a.num_q_tokens);
-  const int q_end = min(max(a.query_start_loc[seq + 1], it.q_begin), a.num_q_tokens);
-  it.ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
+  it.q_begin = min(max(qsl_begin, 0), a.num_q_tokens);
+  const int q_end = min(max(qsl_end, it.q_begin), a.num_q_tokens);
+  it.ctx = max(0, min(context_len, a.ctx_limit));
   it.qlen = min(q_end - it.q_begin, it.ctx);
   it.pos0 = tile * pos_per_tile;
   it.valid = it.qlen > 0 && it.pos0 < it.qlen;
@@ -142,53 +143,197 @@ __device__ inline PrefillItem prefill_item(const PrefillArgs& a, int seq, int ti
   return it;
 }
 
+__device__ inline PrefillItem prefill_item(const PrefillArgs& a, int seq, int tile, int split,
+                                           int pos_per_tile) {
+  return prefill_item_at(a, a.query_start_loc[seq], a.query_start_loc[seq + 1], a.context_lens[seq], tile,
+                         split, pos_per_tile);
+}
+
 // Work plan of one prefill call: every (chunk, row tile, key range) item that
 // has keys, longest key range first (a counting sort over 64 classes), so the
 // dispatcher starts the long items first and fills the tail with short ones.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBuckets = 64;
 
+constexpr int kPlanSeqCache = 4096;  // chunks whose bounds and context lengths the plan keeps in LDS
+
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs a, int32_t pos_per_tile,
                                                                    int32_t ntiles, int32_t nsplit,
-                                                                   int4* plan, int32_t* plan_count) {
+                                                                   int4* plan, int32_t* plan_count,
+                                                                   int32_t* tok_seq) {
   __shared__ int hist[kPlanBuckets];
+  __shared__ int s_qs[kPlanSeqCache];  // query_start_loc as given
+  __shared__ int s_cl[kPlanSeqCache];  // context_lens as given
+  __shared__ int s_off[kPlanSeqCache];  // first row tile of each chunk among all chunks' tiles
+  __shared__ int s_wsum[kPlanThreads / kWave];
   const int tid = threadIdx.x;
+  const int S = a.num_seqs;
   if (tid < kPlanBuckets) hist[tid] = 0;
+  // Every chunk's bounds and context length, read once (the item loops below
+  // visit each chunk ntiles * nsplit times).
+  const bool cached = S + 1 <= kPlanSeqCache;
+  if (cached) {
+    for (int s = tid; s <= S; s += kPlanThreads) {
+      s_qs[s] = a.query_start_loc[s];
+      if (s < S) s_cl[s] = a.context_lens[s];
+    }
+  }
+  __syncthreads();
+  // The chunk of every query token (-1 for tokens outside every chunk), for
+  // the merge kernel; only when key ranges are split.
+  if (tok_seq != nullptr) {
+    auto start = [&](int s) { return min(max(cached ? s_qs[s] : a.query_start_loc[s], 0), a.num_q_tokens); };
+    if (cached) {
+      for (int t = tid; t < a.num_q_tokens; t += kPlanThreads) {
+        if (t < start(0) || t >= start(S)) {
+          tok_seq[t] = -1;
+          continue;
+        }
+        // The last chunk whose start is <= t (the starts do not decrease).
+        int lo = 0, hi = S;  // start(lo) <= t < start(hi)
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (start(mid) <= t) lo = mid; else hi = mid;
+        }
+        tok_seq[t] = lo;
+      }
+    } else {
+      for (int t = tid; t < a.num_q_tokens; t += kPlanThreads) tok_seq[t] = -1;
+      __syncthreads();
+      for (int s = tid; s < S; s += kPlanThreads) {
+        const int b = start(s), e = max(b, start(s + 1));
+        for (int t = b; t < e; ++t) tok_seq[t] = s;
+      }
+    }
+  }
   __syncthreads();
   static_assert((kSplitKeys - 1) >> 4 < kPlanBuckets, "one class per 16 keys");
-  const int64_t n = static_cast<int64_t>(a.num_seqs) * ntiles * nsplit;
-  auto keys = [&](int64_t i, int* seq, int* tile, int* split) {
-    *split = static_cast<int>(i % nsplit);
-    const int64_t r = i / nsplit;
-    *tile = static_cast<int>(r % ntiles);
-    *seq = static_cast<int>(r / ntiles);
-    const PrefillItem it = prefill_item(a, *seq, *tile, *split, pos_per_tile);
-    return it.valid ? it.key_hi - it.key_lo : 0;
+  // Items by (chunk, row tile) pair, one pair per thread: a pair past its
+  // chunk's rows has none, the others one per key range their rows reach.
+  // Items of a whole range (the top class) are counted and placed per wave
+  // (one LDS atomic per wave), the rest one by one.
+  const int lane = tid & (kWave - 1);
+  // With the chunks in LDS, only the row tiles that hold rows are visited:
+  // chunk s has ceil(rows / pos_per_tile) of them (at most ntiles), and
+  // s_off is their exclusive prefix sum (thread t sums chunks 4t .. 4t + 3).
+  int npairs = S * ntiles;  // < 2^31 (host-checked)
+  if (cached) {
+    static_assert(kPlanSeqCache == 4 * kPlanThreads, "four chunks per thread");
+    int nt[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sq = 4 * tid + j;
+      nt[j] = 0;
+      if (sq < S) {
+        const int qb = min(max(s_qs[sq], 0), a.num_q_tokens);
+        const int qe = min(max(s_qs[sq + 1], qb), a.num_q_tokens);
+        const int rows = min(qe - qb, max(0, min(s_cl[sq], a.ctx_limit)));
+        nt[j] = rows > 0 ? min(ntiles, (rows + pos_per_tile - 1) / pos_per_tile) : 0;
+      }
+      sum += nt[j];
+    }
+    int wtotal;
+    const int incl = wave_scan(sum, &wtotal);
+    if (lane == 0) s_wsum[tid / kWave] = wtotal;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanThreads / kWave; ++w) {
+      before += w < tid / kWave ? s_wsum[w] : 0;
+      total += s_wsum[w];
+    }
+    int off = before + incl - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int sq = 4 * tid + j;
+      if (sq < S) s_off[sq] = off;
+      off += nt[j];
+    }
+    npairs = total;
+    __syncthreads();
+  }
+  auto bucket = [](int t) { return kPlanBuckets - 1 - ((t - 1) >> 4); };
+  struct Pair {
+    int seq, tile, s_lo, s_hi;  // key ranges s_lo .. s_hi (none when s_hi < s_lo)
+    int key_lo, key_end;        // the keys the tile's rows see: key_lo (a pass boundary) .. key_end - 1
   };
-  for (int64_t i = tid; i < n; i += kPlanThreads) {
-    int seq, tile, split;
-    const int t = keys(i, &seq, &tile, &split);
-    if (t > 0) atomicAdd(&hist[kPlanBuckets - 1 - ((t - 1) >> 4)], 1);
+  auto pair_of = [&](int pr) {
+    Pair x{};
+    x.s_lo = 0;
+    x.s_hi = -1;
+    if (pr >= npairs) return x;
+    if (cached) {  // the last chunk whose first tile is <= pr
+      int lo = 0, hi = S;  // s_off[lo] <= pr < s_off[hi] (s_off[S] taken as npairs)
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_off[mid] <= pr) lo = mid; else hi = mid;
+      }
+      x.seq = lo;
+      x.tile = pr - s_off[lo];
+    } else {
+      x.seq = pr / ntiles;
+      x.tile = pr - x.seq * ntiles;
+    }
+    const int qb = cached ? s_qs[x.seq] : a.query_start_loc[x.seq];
+    const int qe = cached ? s_qs[x.seq + 1] : a.query_start_loc[x.seq + 1];
+    const int cl = cached ? s_cl[x.seq] : a.context_lens[x.seq];
+    const PrefillItem it = prefill_item_at(a, qb, qe, cl, x.tile, 0, pos_per_tile);
+    if (it.qlen <= 0 || it.pos0 >= it.qlen) return x;  // no rows in this tile
+    const int first_key = a.window > 0 ? max(0, it.ctx - it.qlen + it.pos0 - a.window + 1) : 0;
+    x.s_lo = first_key / kSplitKeys;
+    x.s_hi = it.last_key / kSplitKeys;
+    x.key_lo = first_key & ~(kKeyTile - 1);
+    x.key_end = it.last_key + 1;
+    return x;
+  };
+  // Keys of item (x, split), split in s_lo .. s_hi: the key range of
+  // prefill_item_at, from the pair's bounds.
+  auto keys_of = [&](const Pair& x, int split) {
+    return min((split + 1) * kSplitKeys, x.key_end) - max(split * kSplitKeys, x.key_lo);
+  };
+  for (int p0 = 0; p0 < npairs; p0 += kPlanThreads) {  // uniform trip count: whole waves
+    const Pair x = pair_of(p0 + tid);
+    int top = 0;
+    for (int sp = x.s_lo; sp <= x.s_hi; ++sp) {
+      const int t = keys_of(x, sp);
+      if (t <= 0) continue;
+      if (bucket(t) == 0) ++top;
+      else atomicAdd(&hist[bucket(t)], 1);
+    }
+    int wtop;
+    wave_scan(top, &wtop);
+    if (lane == 0 && wtop > 0) atomicAdd(&hist[0], wtop);
   }
   __syncthreads();
   static_assert(kPlanBuckets == kWave, "one class per lane of wave 0");
-  if (tid < kWave) {
+  if (tid < kWave) {  // wave 0: the classes' offsets (exclusive prefix sum)
     const int c = hist[tid];
-    int incl = c;
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int v = __shfl_up(incl, off, kWave);
-      if (tid >= off) incl += v;
-    }
+    int total;
+    const int incl = wave_scan(c, &total);
     hist[tid] = incl - c;
-    if (tid == kWave - 1) *plan_count = incl;
+    if (tid == 0) *plan_count = total;
   }
   __syncthreads();
-  for (int64_t i = tid; i < n; i += kPlanThreads) {
-    int seq, tile, split;
-    const int t = keys(i, &seq, &tile, &split);
-    if (t <= 0) continue;
-    const int pos = atomicAdd(&hist[kPlanBuckets - 1 - ((t - 1) >> 4)], 1);
-    plan[pos] = make_int4(seq, tile, split, t);
+  for (int p0 = 0; p0 < npairs; p0 += kPlanThreads) {
+    const Pair x = pair_of(p0 + tid);
+    int top = 0;
+    for (int sp = x.s_lo; sp <= x.s_hi; ++sp) {
+      const int t = keys_of(x, sp);
+      if (t > 0 && bucket(t) == 0) ++top;
+    }
+    // This lane's top-class items go to base + (the top items of the lanes
+    // below it) + 0, 1, ...
+    int wtop;
+    const int below = wave_scan(top, &wtop);  // inclusive
+    int base = 0;
+    if (lane == 0 && wtop > 0) base = atomicAdd(&hist[0], wtop);
+    int pos_top = __builtin_amdgcn_readfirstlane(base) + below - top;
+    for (int sp = x.s_lo; sp <= x.s_hi; ++sp) {
+      const int t = keys_of(x, sp);
+      if (t <= 0) continue;
+      const int pos = bucket(t) == 0 ? pos_top++ : atomicAdd(&hist[bucket(t)], 1);
+      plan[pos] = make_int4(x.seq, x.tile, sp, t);
+    }
   }
 }
 
@@ -715,27 +860,30 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
   }
 }
 
-// One wave per (query token, head): merge the key-range
-// partials of rows whose keys spanned more than one range.  Each wave issues
-// its loads in two rounds (the chunk's bounds, then up to four ranges' states
-// at once), so the kernel costs a few memory latencies.
+// One wave per (query token, head): merge the key-range partials of rows
+// whose keys spanned more than one range.  Each wave issues its loads in
+// three rounds (the token's chunk from the plan's map, the chunk's bounds,
+// then up to four ranges' states at once), so the kernel costs a few memory
+// latencies.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(PrefillArgs a, int32_t nsplit,
-                                                                int32_t blocks_per_seq,
+                                                                const int32_t* tok_seq,
                                                                 const float* ws_max,
                                                                 const float* ws_sum,
                                                                 const float* ws_acc) {
   constexpr int PER = D / 64;
-  const int seq = static_cast<int>(blockIdx.x) / blocks_per_seq;  // each chunk's rows in blocks_per_seq blocks
+  const int64_t rowid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  if (rowid >= static_cast<int64_t>(a.num_q_tokens) * a.num_heads) return;
+  const int t = static_cast<int>(rowid / a.num_heads);
+  const int seq = tok_seq[t];
+  if (seq < 0) return;
   const int q_begin = min(max(a.query_start_loc[seq], 0), a.num_q_tokens);
   const int q_end = min(max(a.query_start_loc[seq + 1], q_begin), a.num_q_tokens);
   const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
   const int qlen = min(q_end - q_begin, ctx);
-  const int r = (static_cast<int>(blockIdx.x) - seq * blocks_per_seq) * 4 + static_cast<int>(threadIdx.x >> 6);  // row of the chunk
-  const int pos = r / a.num_heads;
+  const int pos = t - q_begin;
   if (pos >= qlen) return;
-  const int64_t rowid = static_cast<int64_t>(q_begin + pos) * a.num_heads + (r - pos * a.num_heads);
   const int row_lim = ctx - qlen + pos;
   // Key ranges holding the row's keys (those of its window, or 0 .. row_lim).
   const int p0 = a.window > 0 ? max(0, row_lim - a.window + 1) / kSplitKeys : 0;
@@ -812,8 +960,9 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
   float* ws_acc = nsplit > 1 ? reinterpret_cast<float*>(base + w.off_acc) : nullptr;
   int4* plan = reinterpret_cast<int4*>(base + w.off_plan);
   int32_t* plan_count = reinterpret_cast<int32_t*>(base + w.off_count);
+  int32_t* tok_seq = nsplit > 1 ? reinterpret_cast<int32_t*>(base + w.off_tokseq) : nullptr;
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, pos_per_tile, ntiles,
-                     nsplit, plan, plan_count);
+                     nsplit, plan, plan_count, tok_seq);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // An E4M3 cache's K scale folds into the score scale.
@@ -835,12 +984,11 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
   });
   err = hipGetLastError();
   if (err != hipSuccess || nsplit <= 1) return err;
-  const int64_t blocks_per_seq = (static_cast<int64_t>(a.max_query_len) * a.num_heads + 3) / 4;
-  const int64_t blocks = blocks_per_seq * a.num_seqs;
-  if (blocks == 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_merge_kernel<E, D>), dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                     stream, a, nsplit, static_cast<int32_t>(blocks_per_seq), ws_max, ws_sum, ws_acc);
+  const int64_t rows = static_cast<int64_t>(a.num_q_tokens) * a.num_heads;
+  if (rows == 0) return hipSuccess;
+  if ((rows + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_merge_kernel<E, D>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(kThreads), 0,
+                     stream, a, nsplit, tok_seq, ws_max, ws_sum, ws_acc);
   return hipGetLastError();
 }
 
@@ -879,6 +1027,10 @@ PrefillWorkspace prefill_workspace_layout(int32_t num_q_tokens, int32_t num_head
   w.off_count = off;
   w.off_plan = off + 256;
   w.bytes = w.off_plan + align256p(static_cast<size_t>(num_seqs) * ntiles * nsplit * sizeof(int4));
+  if (nsplit > 1) {
+    w.off_tokseq = w.bytes;
+    w.bytes += align256p(static_cast<size_t>(num_q_tokens) * sizeof(int32_t));
+  }
   return w;
 }
 

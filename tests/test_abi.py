@@ -252,9 +252,11 @@ def test_workspace_sizes(lib):
     g = lib.pa_prefill_workspace_bytes
     # One key range: only the work plan, one 16-byte item per (chunk, 16-position tile).
     assert g(2048, 4, 8, 1, 256, 512, 1024) == 256 + a256(4 * 32 * 16)
-    # Four key ranges: max, sum and D partial floats per (token, head, range), then the plan.
+    # Four key ranges: max, sum and D partial floats per (token, head, range), the plan,
+    # then each query token's chunk.
     n = 2048 * 8 * 4
-    assert g(2048, 4, 8, 1, 256, 512, 4096) == 2 * a256(n * 4) + a256(n * 256 * 4) + 256 + a256(4 * 32 * 4 * 16)
+    assert g(2048, 4, 8, 1, 256, 512, 4096) == (2 * a256(n * 4) + a256(n * 256 * 4) + 256
+                                                + a256(4 * 32 * 4 * 16) + a256(2048 * 4))
     assert g(2048, 4, 8, 3, 256, 512, 4096) == 0  # heads not a multiple of KV heads
 
 
