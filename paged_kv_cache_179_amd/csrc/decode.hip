@@ -371,7 +371,15 @@ hipError_t launch_partitions_e(const DecodeArgs& a, hipStream_t stream) {
 // a member's own items start after its shared partitions, and the reduce
 // merges its row.  Which sequences share a group item changes no result: the
 // group path computes each query row on its own.
-constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreads = 1024;  // the most threads; a launch uses plan_threads(num_seqs)
+// Threads of one plan launch: one per sequence, in whole waves, at least 256
+// (wave 0 scans the class histogram, the first 192 threads clear it).  Every
+// wave runs every phase, so spare waves only add issue time (tinyllama's plan
+// took 7.8 us with 1,024 threads for 64 sequences).
+inline int plan_threads(int num_seqs) {
+  const int t = (num_seqs + kWave - 1) / kWave * kWave;
+  return t < 256 ? 256 : (t > kPlanThreads ? kPlanThreads : t);
+}
 constexpr int kPlanBuckets = 64;
 constexpr int kSpanTokens = 2048;
 constexpr int kPlanCtxCache = 8192;  // context lengths kept in LDS
@@ -394,6 +402,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
   __shared__ int s_key1[kShareMaxSeqs];  // and of the next partition, read ahead
   __shared__ int s_ngroup, s_nmem, s_more, s_hit;
   const int tid = threadIdx.x;
+  const int nthr = static_cast<int>(blockDim.x);  // whole waves, >= 256
   const bool share = !WIN && a.share != 0;
   const int P = a.part_tokens;
   const int64_t mbps = a.max_blocks_per_seq;
@@ -402,7 +411,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     s_ngroup = 0;
     s_nmem = 0;
   }
-  for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+  for (int s = tid; s < a.num_seqs; s += nthr) {
     // The context length and, for the search, the first block id: loads
     // issued together, one round trip.
     const int cl = a.context_lens[s];
@@ -428,7 +437,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     while ((1 << hbits) < 2 * a.num_seqs) ++hbits;
     const int hsize = 1 << hbits;
     for (int p = 0; p + 1 < a.num_parts; ++p) {  // a shared partition is never a sequence's last
-      for (int i = tid; i < hsize; i += kPlanThreads) {
+      for (int i = tid; i < hsize; i += nthr) {
         h_key[i] = -1;
         h_lead[i] = 0x7fffffff;
         h_cnt[i] = 0;
@@ -439,7 +448,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
         s_hit = 0;
       }
       __syncthreads();
-      for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+      for (int s = tid; s < a.num_seqs; s += nthr) {
         int slot = -1;
         const int key = s_key[s];
         if (s_qs[s] == p && s_ctx[s] > (p + 1) * P && key >= 0 && key < a.num_blocks) {
@@ -459,7 +468,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
       }
       __syncthreads();
       if (s_hit == 0) break;  // no partition begins with another's block: nothing shared
-      for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+      for (int s = tid; s < a.num_seqs; s += nthr) {
         const int slot = s_slot[s];
         if (slot < 0) continue;
         const int lead = h_lead[slot];
@@ -482,7 +491,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
         else s_slot[s] = -1;  // first block alike, the rest not: read on its own
       }
       __syncthreads();
-      for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+      for (int s = tid; s < a.num_seqs; s += nthr) {
         const int slot = s_slot[s];
         if (slot < 0 || h_lead[slot] != s || h_cnt[slot] == 0) continue;
         // A group's leader reserves its member run and its items: runs of
@@ -499,7 +508,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
         }
       }
       __syncthreads();
-      for (int s = tid; s < a.num_seqs; s += kPlanThreads) {
+      for (int s = tid; s < a.num_seqs; s += nthr) {
         const int slot = s_slot[s];
         if (slot < 0 || h_cnt[slot] == 0) continue;  // not shared at this level
         a.members[h_off[slot] + atomicAdd(&h_fill[slot], 1)] = s;
@@ -513,7 +522,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
       if (s_more == 0) break;
     }
     if (s_ngroup > 0)
-      for (int s = tid; s < a.num_seqs; s += kPlanThreads) a.seq_shared[s] = s_qs[s];
+      for (int s = tid; s < a.num_seqs; s += nthr) a.seq_shared[s] = s_qs[s];
   }
   const int ngroup = share ? s_ngroup : 0;
 
@@ -561,13 +570,13 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     return o.c == 0 ? 1 : (o.c - o.base + (P << k) - 1) / (P << k);
   };
   const int lane = tid & (kWave - 1);
-  const int nloop = (a.num_seqs + kPlanThreads - 1) / kPlanThreads;  // whole waves in step
+  const int nloop = (a.num_seqs + nthr - 1) / nthr;  // whole waves in step
 
   // 1. Item counts of each span choice (wave sums, one atomic per wave).
   if (tid < 3) s_tot[tid] = 0;
   __syncthreads();
   for (int i = 0; i < nloop; ++i) {
-    const int s = i * kPlanThreads + tid;
+    const int s = i * nthr + tid;
     const bool live = s < a.num_seqs;
     const Own o = own(live ? s : 0);
     for (int k = 1; k <= max_k; ++k) {
@@ -598,7 +607,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
     return x;
   };
   for (int i = 0; i < nloop; ++i) {
-    const int s = i * kPlanThreads + tid;
+    const int s = i * nthr + tid;
     const bool live = s < a.num_seqs;
     const Spans x = spans(own(live ? s : 0));
     int total;
@@ -628,7 +637,7 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
   // items take one run (one atomic), each lane its part by a prefix sum.
   const int64_t cap = static_cast<int64_t>(a.num_seqs) * a.num_parts;  // plan entries
   for (int i = 0; i < nloop; ++i) {
-    const int s = i * kPlanThreads + tid;
+    const int s = i * nthr + tid;
     const bool live = s < a.num_seqs;
     const Own o = own(live ? s : 0);
     const Spans x = spans(o);
@@ -734,9 +743,9 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
                    bpp % 4 == 0) ? 1 : 0;
   }
   if (a.window > 0)
-    hipLaunchKernelGGL(decode_plan_kernel<true>, dim3(1), dim3(kPlanThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_plan_kernel<true>, dim3(1), dim3(plan_threads(a.num_seqs)), 0, stream, a);
   else
-    hipLaunchKernelGGL(decode_plan_kernel<false>, dim3(1), dim3(kPlanThreads), 0, stream, a);
+    hipLaunchKernelGGL(decode_plan_kernel<false>, dim3(1), dim3(plan_threads(a.num_seqs)), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (mfma) return launch_decode_mfma(a, stream);
