@@ -730,9 +730,10 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
     const int group = a.num_heads / a.num_kv_heads;
     const int per = a.num_kv_heads * ((group + 15) / 16);
     a.plan_min_items = std::max(1, (2 * decode_mfma_grid(a) + per - 1) / per);
-    // Shared partitions: 16-bit caches, whole contexts, one head chunk per
-    // KV head, blocks of 16+ tokens (one scalar table read per pass).
-    a.share = (!a.kv_fp8 && a.window == 0 && group <= 16 && a.num_seqs >= 2 &&
+    // Shared partitions: whole contexts, one head chunk per KV head, blocks
+    // of 16+ tokens (one scalar table read per pass); E4M3 caches only at
+    // head_dim 128 (the kernel's only E4M3 form with a group path).
+    a.share = (a.window == 0 && group <= 16 && a.num_seqs >= 2 && (!a.kv_fp8 || a.head_dim == 128) &&
                a.num_seqs <= kShareMaxSeqs && a.num_parts > 1 && a.log2_block_size >= 4 &&
                a.seq_shared != nullptr && a.members != nullptr) ? 1 : 0;
     a.share_max_members = decode_group_rows(a.head_dim) / group;

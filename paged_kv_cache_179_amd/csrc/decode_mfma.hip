@@ -203,6 +203,11 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
   // E4M3 caches: a pass is half the bytes, so three slots keep two passes in
   // flight (the bytes in flight per wave of the 16-bit kernel).
   constexpr int NS = KV8 ? 3 : 2;
+  // Group units (see below) exist for 16-bit caches and for E4M3 caches at
+  // head_dim 128.  At E4M3 64 and 256 the group path's registers crowd the
+  // regular path's (measured with the path compiled in: TinyLlama-shaped fp8
+  // decode 5% slower, Gemma-shaped 2.5%).
+  constexpr bool kGroupUnits = !KV8 || D == 128;
   __shared__ u32x4 s_kv[kWaves][NS][2][kTile][CNC];
   // E4M3 caches: each wave's value tile of the pass it computes, widened to
   // 16 bits and rotated as the 16-bit value slots are (keys are widened in
@@ -282,7 +287,7 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
     x.ctx = plan[4 * static_cast<int64_t>(j) + 3];
     x.span = span_word & 0xff;
     x.single = (span_word >> 8) & 1;
-    x.group = !KV8 && ((span_word >> 9) & 1);
+    x.group = kGroupUnits && ((span_word >> 9) & 1);
     x.kvh = r / head_chunks;
     const int chunk = r - x.kvh * head_chunks;
     x.h_first = x.kvh * group + chunk * kHeadTile;
@@ -571,83 +576,125 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
     __syncthreads();
   };
 
-  // Group unit (16-bit caches only): one partition that the block tables of
-  // several sequences share, for all their query rows (member m, head j ->
-  // row m * group + j; up to GT row tiles of 16 per wave, so the partition is
-  // read once for up to decode_group_rows(D) rows).  Every wave computes every
-  // pass: wave w still DMAs passes w, w + 4, ... into its own slots, and after
-  // each round of four passes (one barrier) each wave runs its row tiles over
-  // all four.  Query rows come straight from global memory into registers.
-  // A row's running max moves only on its own scores (the rescale factor is
-  // 1 for the other rows of the tile, an exact no-op), so a row's result does
+  // Group units: one partition that the block tables of several sequences
+  // share, for all their query rows (member m, head j -> row m * group + j;
+  // GT row tiles of 16 per wave, so the partition is read once for up to
+  // decode_group_rows(D) rows).  Every wave computes every pass: wave w still
+  // DMAs passes w, w + kWaves, ... into its own slots, and after each round of
+  // kWaves passes (one per wave) each wave runs its row tiles over all of
+  // them.  Query rows come straight from global memory into registers.  A
+  // row's running max moves only on its own scores (the rescale factor is 1
+  // for the other rows of the tile, an exact no-op), so a row's result does
   // not depend on which rows share its tile.  Each wave writes its rows'
   // partition states itself: no merge across waves.
+  //   Per-wave timestamps of a traced copy (16-bit caches, head_dim 128, 112
+  // rows): a round of eight passes takes 10-16 K cycles of computing, each
+  // pass a chain of dependent steps (LDS reads, score MFMAs, max across
+  // lanes, exponentials, p.V MFMAs) of ~1,250 cycles per row tile.  Four
+  // computing waves with two tiles each (half the LDS reads) were slower
+  // (group units 32.6 against 29.5 us), as were two passes per step.
+  constexpr int GCW = kWaves;                                    // computing waves
+  constexpr int GT = decode_group_rows(D) / (GCW * kHeadTile);  // row tiles per wave
+  static_assert(GT >= 1 && GT * GCW * kHeadTile == decode_group_rows(D), "group rows");
+  u32x4 qr[GT][KB];     // score B operands of this lane's row, per tile
+  f32x4 gacc[GT][MT];
+  f32x4 glacc[GT];
+  float gm[GT];
+  int64_t grow[GT];     // this lane's row: sequence * num_heads + head, or -1
+  int gtiles = 0;       // row tiles of the unit (wave-uniform)
+  // Loads this wave's query rows of group unit x and clears their states.
+  // The chunk of a row that lane (hl, g4) supplies to score MFMA kb matches
+  // the key chunk that koff[kb] (k8off for E4M3 keys) gives the same lane.
+  auto group_begin = [&](const Unit& x) {
+    const int rows = x.nh;
+    gtiles = (rows + kHeadTile - 1) / kHeadTile;
+#pragma unroll
+    for (int i = 0; i < GT; ++i) {
+      const int r = (wave + GCW * i) * kHeadTile + hl;
+      grow[i] = -1;
+      if (r < rows) {
+        const int mem = r / group;
+        const int sq = a.members[x.moff + mem];
+        grow[i] = static_cast<int64_t>(sq) * a.num_heads + x.kvh * group + (r - mem * group);
+      }
+      const char* qsrc = qbase + (grow[i] < 0 ? 0 : grow[i]) * RB;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int c = KV8 ? 2 * (4 * (kb / 2) + g4) + (kb & 1) : 4 * kb + g4;
+        qr[i][kb] = grow[i] < 0 ? u32x4{0u, 0u, 0u, 0u} : load16(qsrc + c * 16);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) gacc[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      glacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      gm[i] = -__builtin_inff();
+    }
+  };
+  // One pass of 16 tokens for this wave's row tiles: ka are the keys as score
+  // A operands, vv the values as transposed p.V A operands.
+  auto group_pass = [&](const u32x4 (&ka)[KB], const s16x4 (&vv)[MT]) {
+#pragma unroll
+    for (int i = 0; i < GT; ++i) {
+      if (wave + GCW * i >= gtiles) continue;  // wave-uniform
+      f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sacc = M::qk(ka[kb], qr[i][kb], sacc);
+      float sc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = score(sacc[e]);
+      const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+      const bool up = mx > gm[i] + kLazyMax;  // this row's own decision
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {  // wave-uniform
+        const float alpha = up ? exp2_fast(gm[i] - mx) : 1.f;  // 0 on the first update
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) gacc[i][mt] *= alpha;
+        glacc[i] *= alpha;
+        gm[i] = up ? mx : gm[i];
+      }
+      const u32x2 pb = {M::pack(exp2_fast(sc[0] - gm[i]), exp2_fast(sc[1] - gm[i])),
+                        M::pack(exp2_fast(sc[2] - gm[i]), exp2_fast(sc[3] - gm[i]))};
+      glacc[i] = M::pv(ones, pb, glacc[i]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) gacc[i][mt] = M::pv(__builtin_bit_cast(u32x2, vv[mt]), pb, gacc[i][mt]);
+    }
+  };
+  // The partition states of this wave's rows of group unit x.
+  auto group_store = [&](const Unit& x) {
+    const int part = x.tb / P;
+#pragma unroll
+    for (int i = 0; i < GT; ++i) {
+      if (wave + GCW * i >= gtiles || grow[i] < 0) continue;
+      const int64_t ws = grow[i] * a.num_parts + part;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        f32x4 o = gacc[i][mt];
+        if constexpr (KV8) o *= a.v_scale;  // values were read without their scale
+        *reinterpret_cast<f32x4*>(a.ws_acc + ws * D + 16 * mt + 4 * g4) = o;
+      }
+      if (g4 == 0) {
+        a.ws_max[ws] = gm[i];
+        a.ws_sum[ws] = glacc[i][0];
+      }
+    }
+  };
+
+  // Group unit over 16-bit caches: two slots per wave, so a round's DMA is
+  // issued once the barrier that ends the previous round has passed.
   //   On entry this wave's pass 0 is in flight in `slot`; on exit the next
   // unit's first pass is in flight in `slot` and, for a regular next unit,
   // its query tile has landed in s_q[qb ^ 1] (as after a regular unit).
-  constexpr int GT = decode_group_rows(D) / (kWaves * kHeadTile);  // row tiles per wave
-  static_assert(GT >= 1, "group rows");
   auto group_unit = [&](const Unit& x, const Unit& nx, int& slot, int qb, bool take) {
     if constexpr (!KV8) {
-      const int rows = x.nh;
-      const int ntile = (rows + kHeadTile - 1) / kHeadTile;
-      u32x4 qr[GT][KB];
-      f32x4 gacc[GT][MT];
-      f32x4 glacc[GT];
-      float gm[GT];
-      int64_t grow[GT];  // this lane's row: sequence * num_heads + head, or -1
-#pragma unroll
-      for (int i = 0; i < GT; ++i) {
-        const int r = (wave + kWaves * i) * kHeadTile + hl;
-        grow[i] = -1;
-        if (r < rows) {
-          const int mem = r / group;
-          const int sq = a.members[x.moff + mem];
-          grow[i] = static_cast<int64_t>(sq) * a.num_heads + x.kvh * group + (r - mem * group);
-        }
-        const char* qsrc = qbase + (grow[i] < 0 ? 0 : grow[i]) * RB;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          qr[i][kb] = grow[i] < 0 ? u32x4{0u, 0u, 0u, 0u} : load16(qsrc + (4 * kb + g4) * 16);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) gacc[i][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        glacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        gm[i] = -__builtin_inff();
-      }
-      // One pass (16 keys and values in a slot) for this wave's row tiles.
-      auto gpass = [&](const char* kt) {
-        const char* vt = kt + kTile * RB;
+      group_begin(x);
+      auto gpass = [&](const char* kt) {  // a slot: keys, then values
         u32x4 ka[KB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) ka[kb] = *reinterpret_cast<const u32x4*>(kt + koff[kb]);
         typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
         s16x4 vv[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) vv[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff[mt]));
-#pragma unroll
-        for (int i = 0; i < GT; ++i) {
-          if (wave + kWaves * i >= ntile) continue;  // wave-uniform
-          f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) sacc = M::qk(ka[kb], qr[i][kb], sacc);
-          float sc[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sc[e] = score(sacc[e]);
-          const float mx = max_across_rows(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-          const bool up = mx > gm[i] + kLazyMax;  // this row's own decision
-          if (__builtin_amdgcn_ballot_w64(up) != 0) {  // wave-uniform
-            const float alpha = up ? exp2_fast(gm[i] - mx) : 1.f;  // 0 on the first update
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) gacc[i][mt] *= alpha;
-            glacc[i] *= alpha;
-            gm[i] = up ? mx : gm[i];
-          }
-          const u32x2 pb = {M::pack(exp2_fast(sc[0] - gm[i]), exp2_fast(sc[1] - gm[i])),
-                            M::pack(exp2_fast(sc[2] - gm[i]), exp2_fast(sc[3] - gm[i]))};
-          glacc[i] = M::pv(ones, pb, glacc[i]);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) gacc[i][mt] = M::pv(__builtin_bit_cast(u32x2, vv[mt]), pb, gacc[i][mt]);
-        }
+        for (int mt = 0; mt < MT; ++mt)
+          vv[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(kt + kTile * RB + voff[mt]));
+        group_pass(ka, vv);
       };
       const int npass = (x.te - x.tb) / kTile;  // full partition
       const int nround = (npass + kWaves - 1) / kWaves;  // the last one may be short
@@ -678,19 +725,7 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
         if (nx.mine > 0) wait_vmcnt<2 * NDMA>();
         else wait_vmcnt<0>();
       }
-      const int part = x.tb / P;
-#pragma unroll
-      for (int i = 0; i < GT; ++i) {
-        if (wave + kWaves * i >= ntile || grow[i] < 0) continue;
-        const int64_t ws = grow[i] * a.num_parts + part;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          *reinterpret_cast<f32x4*>(a.ws_acc + ws * D + 16 * mt + 4 * g4) = gacc[i][mt];
-        if (g4 == 0) {
-          a.ws_max[ws] = gm[i];
-          a.ws_sum[ws] = glacc[i][0];
-        }
-      }
+      group_store(x);
       if (take && tid == 0) s_next = 2 * NG + atomicAdd(queue, 1);
       __syncthreads();  // slots free for the next unit; s_next published
     }
@@ -743,12 +778,84 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
       else if (n >= 2 * NDMA) wait_vmcnt<2 * NDMA>();
       else wait_vmcnt<0>();
     };
+    // One pass of 16 E4M3 keys (slot tile kt) and their widened values (vt)
+    // for this wave's group rows.
+    auto gpass8 = [&](const char* kt, const char* vt) {
+      u32x4 ka[KB];
+#pragma unroll
+      for (int j = 0; j < KB / 2; ++j) widen(*reinterpret_cast<const u32x4*>(kt + k8off[j]), ka[2 * j], ka[2 * j + 1]);
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      s16x4 vv[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) vv[mt] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vt + voff[mt]));
+      group_pass(ka, vv);
+    };
+    // Group unit over E4M3 caches.  Before the transposing reads a value tile
+    // must be widened: after the barrier that ends the previous round, each
+    // wave widens the value tile of its own pass of this round into its 16-bit
+    // tile, and a second barrier publishes the four.  Keys are widened in
+    // registers.  Other waves read this wave's slots, so a slot is refilled
+    // only after the barrier that ends the round which read it: before a
+    // round's first barrier the wave's stream runs at most one pass ahead of
+    // the pass it contributes, after it two.
+    auto group_unit8 = [&](bool take) {
+      const Unit& x = cur;
+      group_begin(x);
+      if (wave == 0 && nxt.valid && !nxt.group) {
+        issue_q(nxt, qb ^ 1);
+        q_after = issued;
+      }
+      if (lane == 0) s_part[wave] = csl;  // slot of this wave's pass 0 of x
+      const int npass = (x.te - x.tb) / kTile;  // full partition
+      const int nround = (npass + kWaves - 1) / kWaves;
+      int gs[kWaves];
+      for (int r = 0; r < nround; ++r) {
+        const bool own = r < x.mine;  // this wave's pass r of x is pass `done` of its stream
+        while (issued - done < NS - 1 && issue_next()) {
+        }
+        if (r == 0) wait_vmcnt<0>();  // the query rows too
+        else if (own) wait_upto(2 * NDMA * (issued - done - 1) + (wave == 0 && q_after > done ? NQ : 0));
+        __syncthreads();  // every wave's pass of round r landed; round r - 1 read by every wave
+        if (r == 0) {
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) gs[w] = __builtin_amdgcn_readfirstlane(s_part[w]);
+        }
+        while (issued - done < NS && issue_next()) {
+        }
+        if (own) convert(csl);
+        __syncthreads();  // the widened value tiles of round r
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          if (r * kWaves + w < npass)
+            gpass8(reinterpret_cast<const char*>(&s_kv[w][(gs[w] + r) % NS][0][0][0]),
+                   reinterpret_cast<const char*>(&s_cv[w][0][0]));
+        if (own) {
+          ++done;
+          csl = csl == NS - 1 ? 0 : csl + 1;
+        }
+      }
+      // The next query tile has landed before the barrier below.
+      if (wave == 0 && nxt.valid && !nxt.group) wait_upto(2 * NDMA * (issued - q_after));
+      group_store(x);
+      if (take && tid == 0) s_next = 2 * NG + atomicAdd(queue, 1);
+      __syncthreads();  // slots free for the next unit; s_next published
+    };
     while (true) {
+      if (kGroupUnits && cur.group) {
+        if constexpr (kGroupUnits) group_unit8(queued && nxt.valid);
+        if (!nxt.valid) break;
+        cur = nxt;
+        nxt = info(next_unit());
+        qb ^= 1;
+        ic = in;
+        in = 0;
+        continue;
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       lacc = f32x4{0.f, 0.f, 0.f, 0.f};
       m = -__builtin_inff();
-      if (wave == 0 && nxt.valid) {
+      if (wave == 0 && nxt.valid && !nxt.group) {
         issue_q(nxt, qb ^ 1);  // older than every pass of nxt
         q_after = issued;
       }
@@ -766,7 +873,7 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
       while (issued - done < NS - 1 && issue_next()) {
       }
       // The next query tile has landed before the merge's barrier.
-      if (wave == 0 && nxt.valid) wait_upto(2 * NDMA * (issued - q_after));
+      if (wave == 0 && nxt.valid && !nxt.group) wait_upto(2 * NDMA * (issued - q_after));
       // At most the two slots from csl on are in flight; the one before is free.
       finish(cur, csl == 0 ? NS - 1 : csl - 1, queued && nxt.valid);
       if (!nxt.valid) break;

@@ -16,8 +16,9 @@ constexpr int kMaxHeadsPerWg = 8;    // query heads of one KV head handled by on
 constexpr int kShareMaxSeqs = 2048;  // decode calls of at most this many sequences look for shared partitions
 // Query rows of one group work unit of the MFMA decode kernel (all the
 // sequences of a shared partition, times the group's query heads): one
-// 16-row tile per wave of its workgroup (eight waves at head_dim 128, four at
-// 64 and 256; group units only arise with 16-bit caches).
+// 16-row tile per wave of its workgroup at head_dim 64 and 256 (four waves)
+// and at 128 over 16-bit caches (eight waves); two per wave at 128 over E4M3
+// caches (four waves), the only E4M3 head_dim with group units.
 constexpr int decode_group_rows(int head_dim) { return head_dim == 128 ? 128 : 64; }
 
 struct CacheWriteArgs {

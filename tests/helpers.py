@@ -141,3 +141,19 @@ def read_plan(w, ws, part):
     if P <= 1:
         return P, count, plan, None, None
     return P, count, plan, i32(lay["shared"], S), i32(lay["members"], S * P)
+
+
+def share(w, groups, shared_tokens):
+    """Rewrite w's tables so that each run of sequences in `groups` (lists of
+    decode-row indices, consecutive) names its first member's blocks for its
+    first shared_tokens[g] tokens (whole blocks).  Members must have tokens
+    after the shared part, so that their new token (the last one) stays in a
+    block of their own."""
+    bs = w.block_size
+    for members, n in zip(groups, shared_tokens):
+        ctx = w.context_lens[w.decode_rows[members]]
+        assert (ctx > n).all(), "every member needs tokens after the shared prefix"
+        lead = w.decode_rows[members[0]]
+        for m in members[1:]:
+            w.block_tables[w.decode_rows[m], :n // bs] = w.block_tables[lead, :n // bs]
+    return w

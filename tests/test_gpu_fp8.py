@@ -12,7 +12,7 @@ import torch
 import oracle
 import paged_kv_cache_179_amd as pa
 from paged_kv_cache_179_amd import workloads as W
-from tests.helpers import TOL, f64, max_err, oracle_decode_per_seq, to_dev
+from tests.helpers import TOL, f64, max_err, oracle_decode_per_seq, read_plan, share, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -129,6 +129,53 @@ def test_fp8_decode_halves_and_variants(gpu):
                               w.context_lens[seqs], w.scale, w.block_size, softcap=15.0,
                               window=700)
     assert max_err(full, ref) <= TOL["bf16"]
+
+
+SHARED = [("bf16", 28, 4, 128), ("fp16", 16, 2, 64), ("bf16", 8, 1, 256), ("fp16", 4, 4, 128)]
+
+
+@pytest.mark.parametrize("case", SHARED, ids=[f"{c[0]}-h{c[1]}x{c[2]}-d{c[3]}" for c in SHARED])
+@pytest.mark.parametrize("part", [512, 64])
+def test_fp8_decode_shared_prefix(gpu, case, part):
+    """Decode over E4M3 caches whose tables share prefixes (runs of 16, 2, 7
+    and 6 sequences sharing 512, 1,024, 192 and 128 tokens): the plan holds
+    group items (at head_dim 128 only), the two halves give pa_decode's output
+    bit for bit, and the output matches the oracle over the dequantised
+    pools."""
+    dtype, hq, hkv, d_ = case
+    say(f"fp8 shared prefix {case} part={part}")
+    w = W.small_case(1400 + hq + d_, num_seqs=40, ctx_lo=1, ctx_hi=1400, num_heads=hq,
+                     num_kv_heads=hkv, head_dim=d_, block_size=16, dtype=dtype,
+                     extra_ctx=[1030 + 37 * i for i in range(31)])
+    groups = [list(range(0, 16)), list(range(16, 18)), list(range(18, 25)), [25, 26, 27, 28, 29, 30]]
+    w = share(w, groups, [512, 1024, 192, 128])
+    ks, vs = 0.05, 0.03
+    kc, vc = fp8_case(w, 8, ks, vs)
+    d = to_dev(w, gpu)
+    kd, vd = torch.from_numpy(kc).to(gpu), torch.from_numpy(vc).to(gpu)
+    maxc = int(w.context_lens[w.decode_rows].max())
+    half = torch.full_like(d["query_decode"], float("nan"))
+    ws = pa.decode_partitions(half, d["query_decode"], kd, vd, d["bt_decode"], d["cl_decode"],
+                              w.scale, maxc, partition_size=part, k_scale=ks, v_scale=vs)
+    pa.decode_reduce(half, d["cl_decode"], w.num_heads, w.head_dim, w.max_blocks_per_seq,
+                     w.block_size, maxc, part, ws)
+    full = torch.full_like(half, float("nan"))
+    pa.decode(full, d["query_decode"], kd, vd, d["bt_decode"], d["cl_decode"], w.scale, maxc,
+              partition_size=part, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    _, count, _, _, _ = read_plan(w, ws, part)
+    if d_ != 128:  # E4M3 group items exist at head_dim 128 only: every row reads its own
+        assert int(count[3]) == 0
+    else:
+        assert int(count[3]) > 0, "no group items"
+    assert torch.equal(full, half)
+    seqs = w.decode_rows
+    ref = oracle.paged_decode(f64(w.query_decode), oracle.fp8_dequantize(kc, ks),
+                              oracle.fp8_dequantize(vc, vs), w.block_tables[seqs],
+                              w.context_lens[seqs], w.scale, w.block_size)
+    err = max_err(full, ref)
+    say(f"  max abs err {err:.3e}, group items {int(count[3])}")
+    assert err <= TOL[dtype]
 
 
 PRE = [("bf16", 8, 1, 256, 16), ("fp16", 16, 4, 128, 16), ("bf16", 14, 2, 64, 16),

@@ -13,29 +13,13 @@ import torch
 
 import paged_kv_cache_179_amd as pa
 from paged_kv_cache_179_amd import workloads as W
-from tests.helpers import TOL, max_err, oracle_decode, read_plan, to_dev, written_caches
+from tests.helpers import TOL, max_err, oracle_decode, read_plan, share, to_dev, written_caches
 
 pytestmark = pytest.mark.gpu
 
 
 def say(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def share(w, groups, shared_tokens):
-    """Rewrite w's tables so that each run of sequences in `groups` (lists of
-    decode-row indices, consecutive) names its first member's blocks for its
-    first shared_tokens[g] tokens (whole blocks).  Members must have tokens
-    after the shared part, so that their new token (the last one) stays in a
-    block of their own."""
-    bs = w.block_size
-    for members, n in zip(groups, shared_tokens):
-        ctx = w.context_lens[w.decode_rows[members]]
-        assert (ctx > n).all(), "every member needs tokens after the shared prefix"
-        lead = w.decode_rows[members[0]]
-        for m in members[1:]:
-            w.block_tables[w.decode_rows[m], :n // bs] = w.block_tables[lead, :n // bs]
-    return w
 
 
 def run(w, gpu, part):
