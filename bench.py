@@ -9,10 +9,16 @@ fp16, contexts U[512, 4096], 512-token partitions); the other four workloads
 are measured the same way and reported under "workloads".
 
 Timing: HIP events on the stream the kernels run on (torch's current stream),
-one pair per kernel, K timed steps after W warm-up steps (per phase: the mean,
-and the median, p10 and p90 over the steps).  Between steps, and
-outside the events, a 512 MiB fill evicts the L2s and the 256 MB last-level
-cache so that every step reads its K/V from HBM.
+K timed steps after W warm-up steps, in three passes of K steps each: the
+whole step between two events (the step time and the headline); the same
+step with one more event where the decode begins (the decode call's time,
+plan + partitions + reduce, as one span); and one event after every phase
+(the per-phase breakdown: write, prefill, partitions, reduce).  An event
+recorded between two launches adds to the time around it, so no figure
+spans an event it does not end on.  Per figure: the mean, and the median,
+p10 and p90 over the steps.  Between steps, and outside the events, a 512 MiB
+fill evicts the L2s and the 256 MB last-level cache so that every step reads
+its K/V from HBM.
 
 Figures:
   value          algorithmic bytes of one step / step time (GB/s); algorithmic
@@ -192,32 +198,63 @@ def decode_plan_counts(st):
 
 
 def measure(step, steps, warmup, flush_buf):
-    """Event-timed phases over `steps` steps (after `warmup`); returns ms lists."""
+    """Event-timed steps over `steps` steps (after `warmup`), in three passes:
+    the step between two events ("step"), the step with an event where the
+    decode begins ("decode": plan + partitions + reduce as one span), and one
+    event after every phase (the phases by name).  Returns ms lists."""
     phases = step.phases()
     for _ in range(warmup):
         flush_buf.zero_()
         for _, fn in phases:
             fn()
     torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    res = {name: [] for name, _ in phases}
+    res["step"] = []
+    # 1. The whole step.
     evs = []
     t0 = time.perf_counter()
     for _ in range(steps):
         flush_buf.zero_()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+        e = [ev(), ev()]
+        e[0].record()
+        for _, fn in phases:
+            fn()
+        e[1].record()
+        evs.append(e)
+    torch.cuda.synchronize()
+    res["_wall_s"] = time.perf_counter() - t0
+    res["step"] = [e[0].elapsed_time(e[1]) for e in evs]
+    # 2. The decode call as one span (the phases before it, then one event).
+    if step.has_dec:
+        first_dec = [name for name, _ in phases].index("partitions")
+        evs = []
+        for _ in range(steps):
+            flush_buf.zero_()
+            e = [ev(), ev(), ev()]
+            e[0].record()
+            for i, (_, fn) in enumerate(phases):
+                if i == first_dec:
+                    e[1].record()
+                fn()
+            e[2].record()
+            evs.append(e)
+        torch.cuda.synchronize()
+        res["decode"] = [e[1].elapsed_time(e[2]) for e in evs]
+    # 3. Every phase.
+    evs = []
+    for _ in range(steps):
+        flush_buf.zero_()
+        e = [ev() for _ in range(len(phases) + 1)]
         e[0].record()
         for i, (_, fn) in enumerate(phases):
             fn()
             e[i + 1].record()
         evs.append(e)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    res = {name: [] for name, _ in phases}
-    res["step"] = []
     for e in evs:
         for i, (name, _) in enumerate(phases):
             res[name].append(e[i].elapsed_time(e[i + 1]))
-        res["step"].append(e[0].elapsed_time(e[-1]))
-    res["_wall_s"] = wall
     return res
 
 
@@ -233,7 +270,7 @@ def summarize(name, w, wk, t, steps):
          "step_bytes": wk["step_bytes"],
          "step_gbs": wk["step_bytes"] / (mean["step"] * 1e-3) / 1e9}
     if "partitions" in mean:
-        dec_ms = mean["partitions"] + mean["reduce"]
+        dec_ms = mean["decode"]
         r["decode_ms"] = dec_ms
         r["decode_gbs"] = wk["decode_bytes"] / (dec_ms * 1e-3) / 1e9
         r["decode_hbm_frac"] = r["decode_gbs"] / HBM_PEAK_GBS

@@ -726,10 +726,10 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
   a.plan_min_items = 0;
   a.share = 0;
   if (mfma) {
-    // Join partitions while every persistent workgroup still gets two units.
+    // Join partitions while every persistent workgroup still gets a unit.
     const int group = a.num_heads / a.num_kv_heads;
     const int per = a.num_kv_heads * ((group + 15) / 16);
-    a.plan_min_items = std::max(1, (2 * decode_mfma_grid(a) + per - 1) / per);
+    a.plan_min_items = std::max(1, (decode_mfma_grid(a) + per - 1) / per);
     // Shared partitions: whole contexts, one head chunk per KV head, blocks
     // of 16+ tokens (one scalar table read per pass); E4M3 caches only at
     // head_dim 128 (the kernel's only E4M3 form with a group path).
