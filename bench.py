@@ -34,7 +34,9 @@ Figures:
                  kernel's rate against the read probe.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME]
-       python bench.py --profile-kernel NAME    (a few launches, for rocprofv3)
+       python bench.py --profile-kernel NAME    (a few launches, for rocprofv3;
+                                                 NAME_fp8: the decode over E4M3 copies
+                                                 of the pools, as fp8_kv_cache runs it)
        python bench.py --copy-probe              (1 GiB device copy, counter scale)
 """
 from __future__ import annotations
@@ -440,10 +442,24 @@ def counter_traffic(workload):
 def profile_kernel(name, launches=5):
     from paged_kv_cache_179_amd import workloads as W
 
-    w = W.make(name)
+    fp8 = name.endswith("_fp8")
+    w = W.make(name[: -len("_fp8")] if fp8 else name)
     st = Step(w, torch.device("cuda:0"))
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda:0")
     st.write()
+    if fp8:  # the decode over E4M3 copies of the pools (per-tensor scale 1/64), as fp8_kv runs it
+        scale = 1.0 / 64
+        kc8 = (st.kc.float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+        vc8 = (st.vc.float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+        torch.cuda.synchronize()
+        for _ in range(launches):
+            flush.zero_()
+            st.pa.decode(st.out_d, st.q_d, kc8, vc8, st.bt_d, st.cl_d, w.scale, st.maxc_d,
+                         partition_size=w.partition_size, workspace=st.ws_d, k_scale=scale,
+                         v_scale=scale)
+        torch.cuda.synchronize()
+        log(f"profiled {launches} fp8 decode launches of {w.name}")
+        return
     for _ in range(launches):
         flush.zero_()
         if st.has_dec:
