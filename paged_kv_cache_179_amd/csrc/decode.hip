@@ -743,12 +743,26 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
     a.share_vec = (reinterpret_cast<uintptr_t>(a.block_tables) % 16 == 0 && a.max_blocks_per_seq % 4 == 0 &&
                    bpp % 4 == 0) ? 1 : 0;
   }
-  if (a.window > 0)
-    hipLaunchKernelGGL(decode_plan_kernel<true>, dim3(1), dim3(plan_threads(a.num_seqs)), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_plan_kernel<false>, dim3(1), dim3(plan_threads(a.num_seqs)), 0, stream, a);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  a.static_plan = 0;
+  if (mfma) {
+    // Small calls: when every (sequence, partition, head chunk) slot has a
+    // workgroup of the persistent grid, each workgroup takes the slot its
+    // index names (empty ones exit at once), and the plan launch -- a third
+    // of such a call -- is left out.  No spans are joined and no shared
+    // partitions are looked for; the counts the reduce reads (one partition
+    // per item, no group items) are written by the partition kernel.
+    const int group = a.num_heads / a.num_kv_heads;
+    const uint64_t slots = decode_grid(a, (group + 15) / 16);
+    a.static_plan = slots <= static_cast<uint64_t>(decode_mfma_grid(a)) ? 1 : 0;
+  }
+  if (!a.static_plan) {
+    if (a.window > 0)
+      hipLaunchKernelGGL(decode_plan_kernel<true>, dim3(1), dim3(plan_threads(a.num_seqs)), 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_plan_kernel<false>, dim3(1), dim3(plan_threads(a.num_seqs)), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (mfma) return launch_decode_mfma(a, stream);
   switch (a.dtype) {
     case PA_DTYPE_F16: return launch_partitions_e<F16>(a, stream);

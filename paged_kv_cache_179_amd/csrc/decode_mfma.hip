@@ -243,7 +243,17 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
   const int g4 = lane >> 4;  // 16-lane row of the wave
 
   const int per = a.num_kv_heads * head_chunks;
-  const int n_units = *scalar_ptr<cint*>(a.plan_count) * per;
+  // Static plan: one slot per (sequence, partition, head chunk), one per
+  // workgroup; workgroup 0 leaves the counts the reduce reads (items of one
+  // partition, no group items).
+  const bool stat = a.static_plan != 0;
+  if (stat && blockIdx.x == 0 && threadIdx.x == 0) {
+    a.plan_count[0] = a.num_seqs * a.num_parts;
+    a.plan_count[1] = 0;
+    a.plan_count[2] = 0;
+    a.plan_count[3] = 0;
+  }
+  const int n_units = stat ? a.num_seqs * a.num_parts * per : *scalar_ptr<cint*>(a.plan_count) * per;
   const int u = blockIdx.x;
   if (u >= n_units) return;
   // Workgroup b of N takes units b and 2 N - 1 - b first.  Launches of more
@@ -257,7 +267,7 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
   // r N + b, or r N + N - 1 - b in odd rounds: over the longest-first plan,
   // one that drew a short unit in one round draws a long one in the next.)
   const int NG = static_cast<int>(gridDim.x);
-  const bool queued = n_units >= kQueueRounds * NG;
+  const bool queued = !stat && n_units >= kQueueRounds * NG;
   int32_t* const queue = a.plan_count + 2;
   int rnd = 1;  // round of nxt
   auto next_unit = [&]() {
@@ -275,6 +285,7 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
   const char* qbase = static_cast<const char*>(a.query);
   cint* plan = scalar_ptr<cint*>(a.plan);  // [item][seq, part, run, ctx]
   cint* tables = scalar_ptr<cint*>(a.block_tables);
+  cint* ctx_lens = scalar_ptr<cint*>(a.context_lens);
   cint* members = scalar_ptr<cint*>(a.members);
 
   auto info = [&](int uu) {
@@ -282,12 +293,31 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
     x.valid = uu < n_units;
     const int j = x.valid ? uu / per : 0;
     const int r = x.valid ? uu - j * per : 0;
-    x.seq = plan[4 * static_cast<int64_t>(j)];
-    const int span_word = plan[4 * static_cast<int64_t>(j) + 2];
-    x.ctx = plan[4 * static_cast<int64_t>(j) + 3];
-    x.span = span_word & 0xff;
-    x.single = (span_word >> 8) & 1;
-    x.group = kGroupUnits && ((span_word >> 9) & 1);
+    int pfirst;     // the item's first partition
+    int members_n = 0;  // group item: its sequences
+    if (stat) {
+      // Partition j % num_parts of sequence j / num_parts, when it holds
+      // attended tokens (a sequence with an empty context keeps partition 0,
+      // whose output rows are zeros).
+      x.seq = j / a.num_parts;
+      pfirst = j - x.seq * a.num_parts;
+      x.ctx = max(0, min(ctx_lens[x.seq], a.ctx_limit));
+      const int p0 = S::kWindow ? window_start(a, x.ctx) / P : 0;
+      const int p1 = max(1, (x.ctx + P - 1) / P);
+      x.valid = x.valid && pfirst >= p0 && pfirst < p1;
+      x.span = 1;
+      x.single = p1 - p0 <= 1;
+      x.group = false;
+    } else {
+      x.seq = plan[4 * static_cast<int64_t>(j)];
+      pfirst = plan[4 * static_cast<int64_t>(j) + 1];
+      const int span_word = plan[4 * static_cast<int64_t>(j) + 2];
+      x.ctx = plan[4 * static_cast<int64_t>(j) + 3];
+      x.span = span_word & 0xff;
+      x.single = (span_word >> 8) & 1;
+      x.group = kGroupUnits && ((span_word >> 9) & 1);
+      members_n = span_word >> 16;
+    }
     x.kvh = r / head_chunks;
     const int chunk = r - x.kvh * head_chunks;
     x.h_first = x.kvh * group + chunk * kHeadTile;
@@ -296,9 +326,9 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
     if (x.group) {  // one head chunk per KV head; rows = members x group
       x.moff = x.seq;
       x.seq = members[x.moff];
-      x.nh = (span_word >> 16) * group;
+      x.nh = members_n * group;
     }
-    const int pb = plan[4 * static_cast<int64_t>(j) + 1] * P;
+    const int pb = pfirst * P;
     x.lo = window_start(a, x.ctx);
     // Passes start on a 16-token boundary so that each one stays inside one
     // block; the tokens before the window in the first pass are masked.
@@ -739,6 +769,7 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
   // overlaps the merge.  Wave 0 also stages the next unit's query rows; those
   // NQ DMAs are ordered before a pass's and waited with it.
   Unit cur = info(u);
+  if (!cur.valid) return;  // a static slot past its sequence's context (workgroup-uniform)
   int qb = 0;
   if (wave == 0 && !cur.group) {
     issue_q(cur, 0);

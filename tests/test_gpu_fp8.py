@@ -166,7 +166,7 @@ def test_fp8_decode_shared_prefix(gpu, case, part):
     _, count, _, _, _ = read_plan(w, ws, part)
     if d_ != 128:  # E4M3 group items exist at head_dim 128 only: every row reads its own
         assert int(count[3]) == 0
-    else:
+    elif part == 64:  # 40 x 23 partitions x 4 KV heads: more slots than any grid, so the plan runs
         assert int(count[3]) > 0, "no group items"
     assert torch.equal(full, half)
     seqs = w.decode_rows

@@ -176,6 +176,50 @@ def test_decode_joined_partitions(gpu, case):
     assert torch.equal(out, half)
 
 
+@pytest.mark.parametrize("case", [("bf16", 32, 4, 64, 0.0, 0), ("fp16", 8, 8, 128, 0.0, 0),
+                                  ("bf16", 8, 1, 256, 0.0, 0), ("bf16", 32, 4, 64, 20.0, 300)],
+                         ids=["bf16-h32x4-d64", "fp16-h8x8-d128", "bf16-h8x1-d256", "bf16-h32x4-d64-cap-win"])
+def test_decode_static_plan(gpu, case):
+    """A call whose (sequence, partition, head chunk) slots all fit the
+    persistent grid runs without the plan kernel: one slot per workgroup,
+    empty slots (past a context, or before a window) exit.  The counts the
+    reduce reads come from the partition kernel (items = slots / head chunks,
+    one partition per item, no group items), every row matches the oracle,
+    and the two halves give pa_decode's output bit for bit.  Contexts of 0,
+    1, a partition's edge and the longest one are included.  Slots: 10
+    sequences x 3 partitions x KV heads, at most 240, under the smallest
+    grid (256 workgroups at head_dim 128 and 256)."""
+    dtype, hq, hkv, d_, cap, win = case
+    say(f"decode static plan {case}")
+    w = W.small_case(400 + hq + d_, num_seqs=10, ctx_lo=1, ctx_hi=1500, num_heads=hq,
+                     num_kv_heads=hkv, head_dim=d_, block_size=16, dtype=dtype,
+                     extra_ctx=[7, 1, 511, 512, 513, 1500])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    d["cl_decode"][0] = 0  # an empty context: zeros
+    maxc = int(w.context_lens[w.decode_rows].max())
+    full = torch.full_like(d["query_decode"], float("nan"))
+    pa.decode(full, d["query_decode"], d["key_cache"], d["value_cache"], d["bt_decode"],
+              d["cl_decode"], w.scale, maxc, partition_size=512, logit_softcap=cap,
+              sliding_window=win)
+    half = torch.full_like(full, float("nan"))
+    ws = pa.decode_partitions(half, d["query_decode"], d["key_cache"], d["value_cache"],
+                              d["bt_decode"], d["cl_decode"], w.scale, maxc, partition_size=512,
+                              logit_softcap=cap, sliding_window=win)
+    pa.decode_reduce(half, d["cl_decode"], hq, d_, w.max_blocks_per_seq, w.block_size, maxc, 512,
+                     ws, sliding_window=win)
+    torch.cuda.synchronize()
+    P, count, _, _, _ = read_plan(w, ws, 512)
+    assert [int(x) for x in count] == [len(w.decode_rows) * P, 0, 0, 0], count
+    assert torch.equal(full, half)
+    assert (full[0] == 0).all(), "empty context"
+    kc, vc = written_caches(w)
+    rows = np.arange(1, len(w.decode_rows))
+    err = max_err(full[1:], oracle_decode(w, kc, vc, rows=rows, softcap=cap, window=win))
+    say(f"  max abs err {err:.3e}")
+    assert err <= TOL[dtype]
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 def test_cache_write_bit_exact(gpu, dtype):
     w = W.small_case(7, num_seqs=9, ctx_lo=1, ctx_hi=200, num_heads=8, num_kv_heads=4,

@@ -59,11 +59,25 @@ def test_shared_prefix_runs(gpu, case, part):
 
 
 def test_long_run(gpu):
-    """140 sequences sharing one 512-token prefix."""
+    """140 sequences sharing one 512-token prefix: two levels of group items
+    (partitions of 256), each split into items of at most 4 members (64 rows
+    at head_dim 64, 16 query heads per KV head)."""
     w = W.small_case(1201, num_seqs=150, ctx_lo=600, ctx_hi=1200, num_heads=32, num_kv_heads=2,
                      head_dim=64, block_size=16, dtype="bf16")  # every context > 512
     w = share(w, [list(range(0, 140))], [512])
-    out = run(w, gpu, 512)
+    d = to_dev(w, gpu)
+    pa.reshape_and_cache(d["new_key"], d["new_value"], d["key_cache"], d["value_cache"],
+                         d["slot_mapping"])
+    out = torch.full_like(d["query_decode"], float("nan"))
+    maxc = int(w.context_lens[w.decode_rows].max())
+    ws = pa.decode_partitions(out, d["query_decode"], d["key_cache"], d["value_cache"],
+                              d["bt_decode"], d["cl_decode"], w.scale, maxc, partition_size=256)
+    pa.decode_reduce(out, d["cl_decode"], w.num_heads, w.head_dim, w.max_blocks_per_seq,
+                     w.block_size, maxc, 256, ws)
+    torch.cuda.synchronize()
+    _, count, _, seq_shared, _ = read_plan(w, ws, 256)
+    assert int(count[3]) == 2 * 35, count  # 140 members / 4 per item, at partitions 0 and 1
+    assert (seq_shared[:140] == 2).all() and (seq_shared[140:] == 0).all()
     kc, vc = written_caches(w)
     assert max_err(out, oracle_decode(w, kc, vc)) <= TOL["bf16"]
 
