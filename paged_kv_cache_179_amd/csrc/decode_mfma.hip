@@ -296,11 +296,18 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
     int pfirst;     // the item's first partition
     int members_n = 0;  // group item: its sequences
     if (stat) {
-      // Partition j % num_parts of sequence j / num_parts, when it holds
-      // attended tokens (a sequence with an empty context keeps partition 0,
-      // whose output rows are zeros).
-      x.seq = j / a.num_parts;
-      pfirst = j - x.seq * a.num_parts;
+      // Slot j: partition p = j / num_seqs of sequence ((j % num_seqs) + p
+      // ceil(num_seqs / num_parts)) % num_seqs, when it holds attended tokens
+      // (a sequence with an empty context keeps partition 0, whose output
+      // rows are zeros).  Workgroups go round-robin to the 8 XCDs and round
+      // each XCD's CUs, so workgroups 256 apart share a CU (the timings here
+      // bear that out): without the rotation by p, partition-major slots of 64 sequences x 4 KV heads
+      // put all four partitions of one sequence on one CU (TinyLlama-shaped
+      // decode 25.8 us against 24.0 with the rotation; sequence-major slots
+      // 26.3 us).
+      pfirst = j / a.num_seqs;
+      x.seq = j - pfirst * a.num_seqs;
+      x.seq = (x.seq + pfirst * ((a.num_seqs + a.num_parts - 1) / a.num_parts)) % a.num_seqs;
       x.ctx = max(0, min(ctx_lens[x.seq], a.ctx_limit));
       const int p0 = S::kWindow ? window_start(a, x.ctx) / P : 0;
       const int p1 = max(1, (x.ctx + P - 1) / P);

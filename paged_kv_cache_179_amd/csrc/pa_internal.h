@@ -82,8 +82,8 @@ struct DecodeArgs {
   int32_t share;           // look for partitions whose blocks several sequences' tables share
   int32_t share_max_members;  // sequences one group item may hold (its query rows fit a unit)
   int32_t share_vec;       // the search may read a partition's block ids 16 bytes at a time
-  int32_t static_plan;     // no plan kernel: unit u is partition (u / per) % num_parts of sequence
-                           // u / per / num_parts (per = KV heads x head chunks), one unit per workgroup
+  int32_t static_plan;     // no plan kernel: one (sequence, partition, head chunk) slot per
+                           // workgroup, partition-major (decode_mfma.hip, Unit info)
   float scale;
   float softcap;           // logit soft-cap; 0 = none
   pa_dtype dtype;          // query, output (and cache unless kv_fp8)
