@@ -390,14 +390,16 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
         int b = tables[trow + (t0 >> lbs)];
         b = (b < 0 || b >= a.num_blocks) ? 0 : b;
         const int64_t head_off = ((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) * CRB;
+        // The block's rows of this KV head as a wave-uniform base, a 32-bit
+        // offset per lane (blocks of at most 256 tokens).
 #pragma unroll
         for (int r = 0; r < NDMA; ++r) {
           const int row = r * CRPI + lane / CNC;
           const int pos = lane % CNC;
           const int t = min(t0 + row, x.te - 1);
-          const int64_t roff = head_off + static_cast<int64_t>(t & off_mask) * CRB;
-          dma16(kbase + roff + ((pos + row * CNC / 16) % CNC) * 16, kd + r * 1024);
-          dma16(vbase + roff + pos * 16, vd + r * 1024);
+          const uint32_t roff = static_cast<uint32_t>(t & off_mask) * CRB;
+          dma16_sv(kbase + head_off, roff + ((pos + row * CNC / 16) % CNC) * 16, kd + r * 1024);
+          dma16_sv(vbase + head_off, roff + pos * 16, vd + r * 1024);
         }
       } else {
 #pragma unroll
@@ -416,7 +418,9 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
       return;
     }
     if (lbs >= 4) {
-      // The 16 tokens lie in one block: one scalar table read per pass.
+      // The 16 tokens lie in one block: one scalar table read per pass.  The
+      // block's rows of this KV head as a wave-uniform base, a 32-bit offset
+      // per lane (blocks of at most 256 tokens).
       int b = tables[trow + (t0 >> lbs)];
       b = (b < 0 || b >= a.num_blocks) ? 0 : b;
       const int64_t head_off = ((static_cast<int64_t>(b) * a.num_kv_heads + x.kvh) << lbs) * RB;
@@ -425,9 +429,9 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
         const int row = r * RPI + lane / NC;
         const int pos = lane % NC;
         const int t = min(t0 + row, x.te - 1);
-        const int64_t roff = head_off + static_cast<int64_t>(t & off_mask) * RB;
-        dma16(kbase + roff + ((pos + G::rot_k(row)) % NC) * 16, kd + r * RPI * RB);
-        dma16(vbase + roff + ((pos + G::rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+        const uint32_t roff = static_cast<uint32_t>(t & off_mask) * RB;
+        dma16_sv(kbase + head_off, roff + ((pos + G::rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+        dma16_sv(vbase + head_off, roff + ((pos + G::rot_v(row)) % NC) * 16, vd + r * RPI * RB);
       }
     } else {
       // Small blocks: each row reads its own table entry (vector loads; the

@@ -35,6 +35,24 @@ __device__ inline void dma16(const void* global, const void* lds) {
                : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(global)
                : "memory", "m0");
 }
+
+// As dma16, with the global address given as a wave-uniform base (an SGPR
+// pair) plus this lane's 32-bit byte offset, so that a lane's address costs
+// one 32-bit VGPR instead of 64-bit arithmetic per transfer.
+__device__ inline void dma16_sv(const void* base, uint32_t lane_off, const void* lds) {
+  const uint32_t off = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)lds));
+  // The lane-read builtin returns int: each half goes back through uint32_t,
+  // or the low half would be sign-extended into the high one.
+  const uint64_t b = static_cast<uint64_t>(reinterpret_cast<uintptr_t>(base));
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32))));
+  const uint64_t bu = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(off)), "v"(lane_off), "s"(bu)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Makes this wave's LDS writes visible to its own later reads (and orders its

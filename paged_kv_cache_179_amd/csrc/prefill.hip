@@ -518,12 +518,13 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
           for (int r = 0; r < NDK; ++r) {
             const int piece = r * 64 + lane;
             if (piece < WKEYS * CNC) {
+              // The block's rows of this KV head as a wave-uniform base and a
+              // 32-bit offset per lane.
               const int key = min(k0 + piece / CNC, key_hi - 1);
-              const int64_t roff =
-                  (((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) | (key & off_mask)) * D +
-                  (piece % CNC) * 16;
-              dma16(kbase + roff, kd + r * 1024);
-              dma16(vbase + roff, vd + r * 1024);
+              const int64_t head_off = ((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) * D;
+              const uint32_t roff = static_cast<uint32_t>(key & off_mask) * D + (piece % CNC) * 16;
+              dma16_sv(kbase + head_off, roff, kd + r * 1024);
+              dma16_sv(vbase + head_off, roff, vd + r * 1024);
             }
           }
         } else {
@@ -549,6 +550,23 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
         int blk = __builtin_amdgcn_readlane(blk_lane, p);
         blk = (blk < 0 || blk >= a.num_blocks) ? 0 : blk;
         const int64_t head_off = ((static_cast<int64_t>(blk) * a.num_kv_heads + kvh) << lbs) * RB;
+        if (!fused) {
+          // The block's rows of this KV head as a wave-uniform base, and a
+          // 32-bit offset per lane (a block of at most 256 tokens holds at most
+          // 128 KiB of one head).
+          const char* kb = kbase + head_off;
+          const char* vb = vbase + head_off;
+#pragma unroll
+          for (int r = 0; r < WKEYS / RPI; ++r) {
+            const int row = wave * WKEYS + r * RPI + lane / NC;  // row of the tile
+            const int pos = lane % NC;
+            const int key = min(k0 + r * RPI + lane / NC, key_hi - 1);
+            const uint32_t roff = static_cast<uint32_t>(key & off_mask) * RB;
+            dma16_sv(kb, roff + ((pos + rot_k(row)) % NC) * 16, kd + r * RPI * RB);
+            dma16_sv(vb, roff + ((pos + rot_v(row)) % NC) * 16, vd + r * RPI * RB);
+          }
+          return;
+        }
 #pragma unroll
         for (int r = 0; r < WKEYS / RPI; ++r) {
           const int row = wave * WKEYS + r * RPI + lane / NC;  // row of the tile
