@@ -666,32 +666,34 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
       static_assert(BO + 16 * RB < 65536, "fits the LDS instruction offset");
       opaque_k();
       // Every key operand of the pass is read before its product, the reads
-      // of the second half during the first half's products, so that their
-      // latencies overlap instead of adding up (an order the scheduler keeps:
-      // left to itself it holds one read in flight at a time, to save registers).
+      // for later products during the earlier ones, so that their latencies
+      // overlap instead of adding up (an order the scheduler keeps: left to
+      // itself it holds one read in flight at a time, to save registers).  The
+      // two halves' score chains alternate, so that each product has two
+      // before its dependence (1% on the Gemma chunks against one chain after
+      // the other, same result bits).
       u32x4 ka[2][KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          ka[h][kb] = *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(kop[kb] + BO + h * 16 * RB));
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          ka[h][kb] = *reinterpret_cast<lds_u32x4*>(static_cast<uintptr_t>(kop[kb] + BO + h * 16 * RB));
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
         for (int t = 0; t < NTW; ++t) s[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int t = 0; t < NTW; ++t) s[h][t] = M::run(ka[h][kb], q[t][kb], s[h][t]);
-        }
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, KB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NTW, 0);
+        if (kb + 2 < KB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, KB * NTW, 0);
     };
     auto smpv = [&](int p, auto b_const, bool full, f32x4 (&s)[2][NTW]) {
       constexpr int B = decltype(b_const)::value;
