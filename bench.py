@@ -440,11 +440,15 @@ def partition_kernel_name(w):
 
 
 def kernel_source_hash():
+    """Hash of the library's sources without their // comments and blank
+    lines: a change to the code invalidates the committed counters, a change
+    to a comment does not."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "paged_kv_cache_179_amd", "csrc"))):
         if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(ROOT, "paged_kv_cache_179_amd", "csrc", f), "rb") as fh:
-                h.update(f.encode() + fh.read())
+            with open(os.path.join(ROOT, "paged_kv_cache_179_amd", "csrc", f), encoding="utf-8") as fh:
+                code = [line.split("//", 1)[0].rstrip() for line in fh]
+            h.update(f.encode() + "\n".join(x for x in code if x).encode())
     return h.hexdigest()[:16]
 
 

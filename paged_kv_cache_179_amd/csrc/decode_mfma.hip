@@ -13,7 +13,8 @@
 //   two passes in flight for E4M3 caches, whose passes are half the bytes).
 //   The block id of a pass comes through a scalar load, so the only
 //   vector-memory operations in flight are the DMAs that the explicit waits
-//   count.
+//   count; the block's rows are the DMA's wave-uniform base, each lane adding
+//   a 32-bit offset.
 // * E4M3 caches: keys are widened to 16 bits in registers, right before the
 //   score MFMAs; values into a per-wave 16-bit tile in LDS that the
 //   transposing reads below use.
@@ -41,11 +42,16 @@
 // The kernel is persistent: as many workgroups as fit on the device, each
 // looping over work units (one (sequence, partition) item of the plan, one KV
 // head, up to 16 of its query heads) of the longest-first plan: statically in
-// alternating order (units b, 2 grid - 1 - b, 2 grid + b, ...), or, in long
-// launches, from the third unit on whichever is next in a device-wide queue.
-// Four waves take the unit's 16-token passes in turn and merge through LDS at
-// the end of the unit; the first pass of the next unit is already in flight
-// by then.
+// alternating order (units b, 2 grid - 1 - b, 2 grid + b, ...), or, in
+// launches of more than one round, from the third unit on whichever is next
+// in a device-wide queue.  Calls small enough that every (sequence,
+// partition, head chunk) slot has a workgroup skip the plan: each workgroup
+// takes the slot its index names (the static plan).  The workgroup's waves
+// (eight at head_dim 128 over 16-bit caches, four otherwise) take the unit's
+// 16-token passes in turn and merge through LDS at the end of the unit; the
+// first pass of the next unit is already in flight by then.  Group units
+// (a partition several sequences' tables share, for all their query rows)
+// are described with their code below.
 #include <algorithm>
 #include <atomic>
 
