@@ -16,9 +16,10 @@
 //   (for MQA, 16 positions x 8 heads).  A wave's rows are 16-row MFMA tiles;
 //   their query rows stay in registers.
 // * Keys go by passes of 32.  Each pass's K and V rows are copied HBM -> LDS by
-//   the gfx950 global-to-LDS DMA, a quarter of the rows by each of four
-//   waves, into one of three or four buffers: the next passes are in flight
-//   while one is computed.
+//   the gfx950 global-to-LDS DMA, an equal share of the rows by every wave
+//   (the block's rows a wave-uniform base, each lane adding a 32-bit offset),
+//   into one of three buffers (four at head_dim 256): the next passes are in
+//   flight while one is computed.
 //   Rows are stored with their 16-byte chunks rotated (K by the row, V by twice
 //   the row) so that the compute reads below are bank-conflict free.
 // * Scores, transposed: S^T = K Q^T (keys x rows).  Lane l of the accumulator
