@@ -293,6 +293,31 @@ pa_status pa_prefill_chunk(void* out, const void* query, const int32_t* query_st
                            pa_dtype dtype, void* stream);
 
 /*
+ * A decode step in one call: the step's slot-mapped cache write
+ * (pa_reshape_and_cache of key/value [num_tokens][num_kv_heads][head_dim],
+ * `dtype`, at the int64 slot_mapping [num_tokens]; negative or out-of-pool
+ * slots are skipped) followed by pa_decode over the written caches, with the
+ * write done in the same launch as the decode's work plan (neither reads what
+ * the other writes), so the step takes one launch fewer than the two calls.
+ * After the call the caches and `out` are those of pa_reshape_and_cache then
+ * pa_decode with the same arguments.  16-bit and fp32 caches (E4M3 caches:
+ * pa_reshape_and_cache_fp8 then pa_decode_fp8).  num_tokens may be 0 (a
+ * plain pa_decode); num_seqs may be 0 (a plain write).  Arguments, workspace
+ * and errors as pa_reshape_and_cache and pa_decode.  (mini-vLLM README,
+ * "End-to-end throughput vs baselines": launch overhead is the dominant cost
+ * for small models, and the new tokens' K/V go into the pool in one scatter.)
+ */
+pa_status pa_decode_fused_write(void* out, const void* query, const void* key, const void* value,
+                                const int64_t* slot_mapping, int32_t num_tokens, void* key_cache,
+                                void* value_cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_context_len, float scale, float logit_softcap,
+                                int32_t sliding_window, int32_t partition_size, void* workspace,
+                                size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/*
  * Chunked prefill with the chunk's own cache write fused in (one call for a
  * mixed step: decode rows are chunks of L = 1).  As pa_prefill_chunk, plus
  * the chunk tokens' new K and V ([num_q_tokens][num_kv_heads][head_dim],

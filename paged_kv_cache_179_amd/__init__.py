@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     PagedAttentionError,
     copy_blocks,
     decode,
+    decode_fused_write,
     decode_noalloc,
     decode_partitions,
     decode_reduce,

@@ -64,6 +64,9 @@ _SIGNATURES = {
                                 _c_ptr, _c_ptr, _i32, _c_ptr, _i32, _i32, _i32, _i32, _i32, _i32,
                                 _i32, _f32, _f32, _i32, _c_ptr, _size, ctypes.c_int, _c_ptr],
                                ctypes.c_int),
+    "pa_decode_fused_write": ([_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr, _c_ptr, _c_ptr,
+                               _i32, _c_ptr, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32,
+                               _i32, _i32, _c_ptr, _size, ctypes.c_int, _c_ptr], ctypes.c_int),
     "pa_prefill_workspace_bytes": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32], _size),
     "pa_prefill_chunk": ([_c_ptr, _c_ptr, _c_ptr, _i32, _i32, _c_ptr, _c_ptr, _c_ptr, _i32, _c_ptr,
                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _c_ptr, _size,
@@ -302,6 +305,36 @@ def decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
         args += list(_scales(key_cache, k_scale, v_scale))
     st = getattr(library(), name)(*args, ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
     _check(name, st)
+    return ws
+
+
+def decode_fused_write(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor,
+                       value: torch.Tensor, slot_mapping: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, block_tables: torch.Tensor,
+                       context_lens: torch.Tensor, scale: float, max_context_len: int,
+                       partition_size: int = 512, workspace: Optional[torch.Tensor] = None,
+                       logit_softcap: float = 0.0, sliding_window: int = 0):
+    """reshape_and_cache of ``key``/``value`` ([T, Hkv, D]) at ``slot_mapping``
+    (int64 [T]) and decode, in one call; see pa_decode_fused_write.  16-bit
+    and fp32 caches."""
+    if _is_fp8(key_cache):
+        raise TypeError("the fused call takes 16-bit or fp32 caches of the query's dtype")
+    ptrs, (nb, hkv, bs, d, s, hq, mbps, dt) = _decode_common(out, query, key_cache, value_cache,
+                                                             block_tables, context_lens)
+    if key.shape != value.shape or key.dim() != 3 or tuple(key.shape[1:]) != (hkv, d):
+        raise ValueError("key/value must be [num_tokens, num_kv_heads, head_dim]")
+    nt = int(key.shape[0])
+    if tuple(slot_mapping.shape) != (nt,):
+        raise ValueError("slot_mapping must be [num_tokens]")
+    need = decode_workspace_bytes(s, hq, d, max_context_len, partition_size)
+    ws, ws_ptr = _workspace(need, out, workspace)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    st = library().pa_decode_fused_write(
+        ptrs[0], ptrs[1], _dev(key, "key", dt), _dev(value, "value", dt),
+        _dev(slot_mapping, "slot_mapping", torch.int64), nt, ptrs[2], ptrs[3], ptrs[4], mbps,
+        ptrs[5], s, hq, hkv, d, bs, nb, int(max_context_len), float(scale), float(logit_softcap),
+        int(sliding_window), int(partition_size), ws_ptr, nbytes, PA_DTYPE[dt], _stream(out))
+    _check("pa_decode_fused_write", st)
     return ws
 
 

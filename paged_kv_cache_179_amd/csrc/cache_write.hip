@@ -16,22 +16,10 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const u32x4* __restrict__ key, const u32x4* __restrict__ value, u32x4* __restrict__ key_cache,
     u32x4* __restrict__ value_cache, const int64_t* __restrict__ slot_mapping, int64_t total,
     int32_t chunks_per_row, int32_t num_kv_heads, int32_t log2_bs, int64_t num_slots) {
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  const int64_t per_token = static_cast<int64_t>(chunks_per_row) * num_kv_heads;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += stride) {
-    const int64_t n = i / per_token;
-    const int64_t rem = i - n * per_token;  // = head * chunks_per_row + chunk
-    const int64_t slot = slot_mapping[n];
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t blk = slot >> log2_bs;
-    const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
-    const int64_t head = rem / chunks_per_row;
-    const int64_t chunk = rem - head * chunks_per_row;
-    const int64_t dst = (((blk * num_kv_heads + head) << log2_bs) + off) * chunks_per_row + chunk;
-    key_cache[dst] = key[i];
-    value_cache[dst] = value[i];
-  }
+  copy_rows_to_cache(key, value, key_cache, value_cache, slot_mapping, total, chunks_per_row,
+                     num_kv_heads, log2_bs, num_slots,
+                     static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x,
+                     static_cast<int64_t>(gridDim.x) * blockDim.x);
 }
 
 // E4M3 byte of y (round to nearest, ties to even), saturating to +-448;

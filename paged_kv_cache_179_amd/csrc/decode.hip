@@ -389,7 +389,7 @@ static_assert(kShareHash >= 2 * kShareMaxSeqs, "hash table load: the search size
 static_assert(kShareMaxSeqs <= kPlanCtxCache, "searched sequences keep their context in LDS");
 
 template <bool WIN>
-__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
+__device__ __forceinline__ void plan_body(const DecodeArgs& a) {
   __shared__ int hist[3][kPlanBuckets];  // per span choice 1, 2, 4
   __shared__ int s_ctx[kPlanCtxCache];
   __shared__ int s_tot[3];  // items per span choice
@@ -661,6 +661,40 @@ __global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a)
   }
 }
 
+template <bool WIN>
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_kernel(DecodeArgs a) {
+  plan_body<WIN>(a);
+}
+
+// The step's new K/V rows for the plan-and-write launch (16-bit and fp32
+// caches; a bit copy, as pa_reshape_and_cache).
+struct WriteRows {
+  const u32x4* key;
+  const u32x4* value;
+  u32x4* key_cache;
+  u32x4* value_cache;
+  const int64_t* slot_mapping;
+  int64_t total;  // 16-byte items: tokens x KV heads x chunks per row
+  int32_t chunks_per_row, num_kv_heads, log2_bs;
+  int64_t num_slots;
+};
+
+// The plan and the step's cache write in one launch: neither reads what the
+// other writes (the plan reads context lengths and block tables only), and
+// the partition kernel after it sees both.  Workgroup 0 plans; the others
+// copy the rows.  Every workgroup carries the plan's LDS, so each holds a CU.
+template <bool WIN>
+__global__ __launch_bounds__(kPlanThreads) void decode_plan_write_kernel(DecodeArgs a, WriteRows w) {
+  if (blockIdx.x == 0) {
+    plan_body<WIN>(a);
+    return;
+  }
+  copy_rows_to_cache(w.key, w.value, w.key_cache, w.value_cache, w.slot_mapping, w.total,
+                     w.chunks_per_row, w.num_kv_heads, w.log2_bs, w.num_slots,
+                     static_cast<int64_t>(blockIdx.x - 1) * blockDim.x + threadIdx.x,
+                     static_cast<int64_t>(gridDim.x - 1) * blockDim.x);
+}
+
 template <typename E, bool WIN>
 hipError_t launch_reduce_w(const DecodeArgs& a, hipStream_t stream) {
   const int64_t rows = static_cast<int64_t>(a.num_seqs) * a.num_heads;
@@ -720,7 +754,12 @@ static bool vector_kernel_forced() {
 }
 
 hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) {
-  if (args.num_seqs <= 0) return hipSuccess;
+  return launch_decode_partitions_write(args, nullptr, stream);
+}
+
+hipError_t launch_decode_partitions_write(const DecodeArgs& args, const CacheWriteArgs* write,
+                                          hipStream_t stream) {
+  if (args.num_seqs <= 0) return write ? launch_reshape_and_cache(*write, stream) : hipSuccess;
   DecodeArgs a = args;
   const bool mfma = a.dtype != PA_DTYPE_F32 && (a.kv_fp8 || !vector_kernel_forced());
   a.plan_min_items = 0;
@@ -755,11 +794,39 @@ hipError_t launch_decode_partitions(const DecodeArgs& args, hipStream_t stream) 
     const uint64_t slots = decode_grid(a, (group + 15) / 16);
     a.static_plan = slots <= static_cast<uint64_t>(decode_mfma_grid(a)) ? 1 : 0;
   }
-  if (!a.static_plan) {
-    if (a.window > 0)
-      hipLaunchKernelGGL(decode_plan_kernel<true>, dim3(1), dim3(plan_threads(a.num_seqs)), 0, stream, a);
-    else
-      hipLaunchKernelGGL(decode_plan_kernel<false>, dim3(1), dim3(plan_threads(a.num_seqs)), 0, stream, a);
+  const int pthreads = plan_threads(a.num_seqs);
+  WriteRows wr{};
+  if (write) {
+    wr.key = static_cast<const u32x4*>(write->key);
+    wr.value = static_cast<const u32x4*>(write->value);
+    wr.key_cache = static_cast<u32x4*>(write->key_cache);
+    wr.value_cache = static_cast<u32x4*>(write->value_cache);
+    wr.slot_mapping = write->slot_mapping;
+    wr.chunks_per_row = write->head_dim * write->elem_bytes / 16;
+    wr.num_kv_heads = write->num_kv_heads;
+    wr.log2_bs = write->log2_block_size;
+    wr.num_slots = static_cast<int64_t>(write->num_blocks) << write->log2_block_size;
+    wr.total = static_cast<int64_t>(write->num_tokens) * write->num_kv_heads * wr.chunks_per_row;
+  }
+  if (a.static_plan) {
+    if (write) {  // no plan to share a launch with
+      const hipError_t e = launch_reshape_and_cache(*write, stream);
+      if (e != hipSuccess) return e;
+    }
+  } else {
+    if (wr.total > 0) {
+      // One copying workgroup per CU at most besides the planner (each holds a CU's LDS).
+      const int64_t need = (wr.total + pthreads - 1) / pthreads;
+      const unsigned copiers = static_cast<unsigned>(std::min<int64_t>(need, 255));
+      if (a.window > 0)
+        hipLaunchKernelGGL(decode_plan_write_kernel<true>, dim3(1 + copiers), dim3(pthreads), 0, stream, a, wr);
+      else
+        hipLaunchKernelGGL(decode_plan_write_kernel<false>, dim3(1 + copiers), dim3(pthreads), 0, stream, a, wr);
+    } else if (a.window > 0) {
+      hipLaunchKernelGGL(decode_plan_kernel<true>, dim3(1), dim3(pthreads), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL(decode_plan_kernel<false>, dim3(1), dim3(pthreads), 0, stream, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

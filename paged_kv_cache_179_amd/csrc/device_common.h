@@ -190,4 +190,30 @@ inline auto with_score_map(float scale, float softcap, int32_t window, F&& launc
   return launch(make_score_map<false, false>(scale, softcap));
 }
 
+// Slot-mapped bit copy of new K/V rows into the pools.  Item i is 16-byte
+// chunk i of the [token][KV head][chunk] inputs; it goes to its token's slot
+// (block slot >> log2_bs, offset slot & (2^log2_bs - 1)) in the
+// [block][KV head][offset][chunk] pools.  Tokens whose slot is negative or
+// past the pool are skipped.  This thread takes items first, first + step, ...
+__device__ inline void copy_rows_to_cache(const u32x4* __restrict__ key, const u32x4* __restrict__ value,
+                                          u32x4* __restrict__ key_cache, u32x4* __restrict__ value_cache,
+                                          const int64_t* __restrict__ slot_mapping, int64_t total,
+                                          int32_t chunks_per_row, int32_t num_kv_heads, int32_t log2_bs,
+                                          int64_t num_slots, int64_t first, int64_t step) {
+  const int64_t per_token = static_cast<int64_t>(chunks_per_row) * num_kv_heads;
+  for (int64_t i = first; i < total; i += step) {
+    const int64_t n = i / per_token;
+    const int64_t rem = i - n * per_token;  // = head * chunks_per_row + chunk
+    const int64_t slot = slot_mapping[n];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t blk = slot >> log2_bs;
+    const int64_t off = slot & ((int64_t(1) << log2_bs) - 1);
+    const int64_t head = rem / chunks_per_row;
+    const int64_t chunk = rem - head * chunks_per_row;
+    const int64_t dst = (((blk * num_kv_heads + head) << log2_bs) + off) * chunks_per_row + chunk;
+    key_cache[dst] = key[i];
+    value_cache[dst] = value[i];
+  }
+}
+
 }  // namespace pa

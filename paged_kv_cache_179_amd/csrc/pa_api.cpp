@@ -430,6 +430,41 @@ pa_status pa_decode(void* out, const void* query, const void* key_cache, const v
   return to_status(pa::launch_decode_reduce(a, s));
 }
 
+pa_status pa_decode_fused_write(void* out, const void* query, const void* key, const void* value,
+                                const int64_t* slot_mapping, int32_t num_tokens, void* key_cache,
+                                void* value_cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                int32_t max_context_len, float scale, float logit_softcap,
+                                int32_t sliding_window, int32_t partition_size, void* workspace,
+                                size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  // The write's checks (as pa_reshape_and_cache), then the decode's.
+  if (num_tokens < 0) return PA_ERR_BAD_SHAPE;
+  if (num_tokens > 0) {
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping) return PA_ERR_NULL_POINTER;
+    if (!aligned(key, 16) || !aligned(value, 16) || !aligned(key_cache, 16) ||
+        !aligned(value_cache, 16) || !aligned(slot_mapping, 8))
+      return PA_ERR_UNSUPPORTED;
+  }
+  pa::DecodeArgs a{};
+  pa_status st = decode_args(out, query, key_cache, value_cache, block_tables, max_blocks_per_seq,
+                             context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, max_context_len, scale, logit_softcap,
+                             sliding_window, partition_size, workspace, workspace_bytes, dtype,
+                             &a);
+  if (st != PA_OK) return st;
+  const pa::CacheWriteArgs w{key, value, key_cache, value_cache, slot_mapping, num_tokens,
+                             num_kv_heads, head_dim, log2i(block_size), num_blocks,
+                             elem_bytes(dtype), dtype, 0, 1.f, 1.f};
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (num_seqs == 0)  // a write only
+    return num_tokens > 0 ? to_status(pa::launch_reshape_and_cache(w, s)) : PA_OK;
+  st = to_status(pa::launch_decode_partitions_write(a, num_tokens > 0 ? &w : nullptr, s));
+  if (st != PA_OK) return st;
+  return to_status(pa::launch_decode_reduce(a, s));
+}
+
 pa_status pa_decode_noalloc(void* out, const void* query, const void* key_cache,
                             const void* value_cache, const int32_t* block_tables,
                             int32_t max_blocks_per_seq, const int32_t* context_lens,

@@ -144,6 +144,11 @@ hipError_t launch_block_copy(const BlockCopyArgs& a, hipStream_t stream);
 constexpr int64_t kProbeSpan = 256 * 1024;
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_decode_partitions(const DecodeArgs& a, hipStream_t stream);
+// As launch_decode_partitions, with the step's cache write (16-bit or fp32
+// caches, write->kv_fp8 == 0) done in the plan's launch, or, for a call with
+// the static plan, in a launch of its own first.
+hipError_t launch_decode_partitions_write(const DecodeArgs& a, const CacheWriteArgs* write,
+                                          hipStream_t stream);
 // 16-bit caches: the MFMA kernel (decode_mfma.hip), any group size.
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 // Workgroups one launch of the MFMA kernel keeps resident (its persistent grid).

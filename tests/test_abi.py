@@ -194,6 +194,23 @@ def test_decode_validation(lib, fn):
     assert decode(lib, fn, s=0, out=N, q=N, kc=N, vc=N, bt=N, cl=N) == OK
 
 
+def test_decode_fused_write_validation(lib):
+    """The write's checks, then pa_decode's (no GPU call on any of these)."""
+    f = lambda key=P, value=P, slots=P, nt=4, s=4, kc=P, out=P, ws=P, dt=F16: \
+        lib.pa_decode_fused_write(out, P, key, value, slots, nt, kc, P, P, 100, P, s, 8, 2, 128, 16,
+                                  64, 1000, 0.1, 0.0, 0, 512, ws, 1 << 30, dt, N)
+    assert f(nt=-1) == SHAPE
+    assert f(key=N) == NULLP
+    assert f(slots=N) == NULLP
+    assert f(kc=N) == NULLP
+    assert f(value=ctypes.c_void_p((1 << 20) + 8)) == UNSUP
+    assert f(slots=ctypes.c_void_p((1 << 20) + 4)) == UNSUP
+    assert f(dt=3) == UNSUP
+    assert f(out=N) == NULLP        # the decode's own checks
+    assert f(ws=N) == NULLP         # 2 partitions need a workspace
+    assert f(nt=0, key=N, value=N, slots=N, s=0, out=N) == OK  # nothing to do
+
+
 def decode_noalloc(lib, out=P, q=P, kc=P, vc=P, bt=P, mbps=100, cl=P, s=4, hq=8, hkv=2, d=128,
                    bs=16, nb=64, maxc=1000, scale=0.1, cap=0.0, win=0, part=512, dt=F16):
     return lib.pa_decode_noalloc(out, q, kc, vc, bt, mbps, cl, s, hq, hkv, d, bs, nb, maxc, scale,

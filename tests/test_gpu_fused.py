@@ -1,7 +1,9 @@
 """GPU parity of the fused chunk write (pa_prefill_chunk_fused): its output is
 bitwise that of the cache write followed by the plain prefill, the caches
 afterwards are bitwise the oracle's write, and a whole mixed step (chunks plus
-decode rows as one-token chunks) in one call matches the oracle."""
+decode rows as one-token chunks) in one call matches the oracle.  Likewise the
+one-call decode step (pa_decode_fused_write) against the write followed by
+pa_decode."""
 from __future__ import annotations
 
 import sys
@@ -13,7 +15,8 @@ import torch
 import oracle
 import paged_kv_cache_179_amd as pa
 from paged_kv_cache_179_amd import workloads as W
-from tests.helpers import TOL, f64, max_err, oracle_decode, oracle_prefill, raw, to_dev
+from tests.helpers import (TOL, f64, max_err, oracle_decode, oracle_prefill, raw, to_dev,
+                           written_caches)
 
 pytestmark = pytest.mark.gpu
 
@@ -99,3 +102,64 @@ def test_mixed_step_in_one_call(gpu, case):
     nq = int(w.query_start_loc[-1])
     assert max_err(out[:nq], oracle_prefill(w, kt, vt)) <= TOL[case[0]]
     assert max_err(out[nq:], oracle_decode(w, kt, vt)) <= TOL[case[0]]
+
+
+DEC_CASES = [("bf16", 28, 4, 128, 16), ("fp16", 32, 4, 64, 16), ("fp32", 4, 2, 64, 16),
+             ("bf16", 8, 1, 256, 32)]
+
+
+@pytest.mark.parametrize("case", DEC_CASES, ids=[f"{c[0]}-h{c[1]}x{c[2]}-d{c[3]}-bs{c[4]}" for c in DEC_CASES])
+@pytest.mark.parametrize("part", [512, 64])
+@pytest.mark.parametrize("variant", [(0.0, 0), (20.0, 300)], ids=["plain", "cap20-win300"])
+def test_decode_fused_write_equals_write_then_decode(gpu, case, part, variant):
+    """pa_decode_fused_write against pa_reshape_and_cache then pa_decode on
+    copies of the same pools: caches and output bit for bit, with one token's
+    slot negative and one past the pool (both skipped).  The shapes take the
+    plan-and-write launch (the plan path) and, for the small ones at
+    partitions of 512, the static plan with the write in a launch of its own;
+    fp32 runs the vector kernel.  The plain case at partitions of 512 is also
+    compared with the oracle."""
+    dtype, hq, hkv, d_, bs = case
+    cap, win = variant
+    say(f"decode fused write {case} part={part} {variant}")
+    w = W.small_case(500 + hq + d_ + bs, num_seqs=40, ctx_lo=1, ctx_hi=1500, num_heads=hq,
+                     num_kv_heads=hkv, head_dim=d_, block_size=bs, dtype=dtype,
+                     extra_ctx=[1, 2, 16, 17, 512, 513, 1500])
+    d = to_dev(w, gpu)
+    maxc = int(w.context_lens[w.decode_rows].max())
+    num_slots = w.num_blocks * w.block_size
+    slots = d["slot_mapping"].clone()
+    slots[3] = -1
+    slots[5] = num_slots + 7
+
+    def run(fused, sl):
+        kc, vc = d["key_cache"].clone(), d["value_cache"].clone()
+        out = torch.full_like(d["query_decode"], float("nan"))
+        if fused:
+            pa.decode_fused_write(out, d["query_decode"], d["new_key"], d["new_value"], sl, kc, vc,
+                                  d["bt_decode"], d["cl_decode"], w.scale, maxc,
+                                  partition_size=part, logit_softcap=cap, sliding_window=win)
+        else:
+            pa.reshape_and_cache(d["new_key"], d["new_value"], kc, vc, sl)
+            pa.decode(out, d["query_decode"], kc, vc, d["bt_decode"], d["cl_decode"], w.scale,
+                      maxc, partition_size=part, logit_softcap=cap, sliding_window=win)
+        torch.cuda.synchronize()
+        return out, kc, vc
+
+    o1, k1, v1 = run(False, slots)
+    o2, k2, v2 = run(True, slots)
+    # bytes, not values: the skipped tokens' slots keep the workload's NaN fill
+    assert torch.equal(k1.view(torch.uint8), k2.view(torch.uint8)), "key caches differ"
+    assert torch.equal(v1.view(torch.uint8), v2.view(torch.uint8)), "value caches differ"
+    # rows 3 and 5 attend their own unwritten (NaN-filled) slot: loud, as designed
+    live = torch.ones(o2.shape[0], dtype=torch.bool, device=o2.device)
+    live[[3, 5]] = False
+    assert torch.isfinite(o2[live]).all()
+    assert not torch.isfinite(o2[3]).all() and not torch.isfinite(o2[5]).all()
+    assert torch.equal(o1.view(torch.uint8), o2.view(torch.uint8)), "outputs differ"
+    if part == 512 and cap == 0.0:
+        o3, _, _ = run(True, d["slot_mapping"])
+        kc, vc = written_caches(w)
+        err = max_err(o3, oracle_decode(w, kc, vc))
+        say(f"  max abs err {err:.3e}")
+        assert err <= TOL[dtype]
