@@ -10,10 +10,13 @@ are measured the same way and reported under "workloads".
 
 Timing: HIP events on the stream the kernels run on (torch's current stream),
 K timed steps after W warm-up steps, in three passes of K steps each: the
-whole step between two events (the step time and the headline); the same
-step with one more event where the decode begins (the decode call's time,
-plan + partitions + reduce, as one span); and one event after every phase
-(the per-phase breakdown: write, prefill, partitions, reduce).  An event
+whole step between two events, in its one-call form (pa_decode_fused_write:
+the step's cache write done in the decode's plan launch; then the prefill
+chunks of a mixed step) -- the step time and the headline; the step as
+separate calls with one more event where the decode begins (the decode
+call's time, plan + partitions + reduce, as one span); and the separate
+calls with one event after every phase (the per-phase breakdown: write,
+prefill, partitions, reduce).  An event
 recorded between two launches adds to the time around it, so no figure
 spans an event it does not end on.  Per figure: the mean, and the median,
 p10 and p90 over the steps.  Between steps, and outside the events, a 512 MiB
@@ -163,6 +166,20 @@ class Step:
     def write(self):
         self.pa.reshape_and_cache(self.nk, self.nv, self.kc, self.vc, self.slots)
 
+    def one_call_step(self):
+        """The step in the fewest launches: every new token's cache write done
+        in the decode call's plan launch (pa_decode_fused_write), then, for a
+        mixed step, the prefill chunks."""
+        w = self.w
+        if self.has_dec:
+            self.pa.decode_fused_write(self.out_d, self.q_d, self.nk, self.nv, self.slots, self.kc,
+                                       self.vc, self.bt_d, self.cl_d, w.scale, self.maxc_d,
+                                       partition_size=w.partition_size, workspace=self.ws_d)
+        else:
+            self.write()
+        if self.has_pre:
+            self.prefill()
+
     def partitions(self):
         self.pa.decode_partitions(self.out_d, self.q_d, self.kc, self.vc, self.bt_d, self.cl_d,
                                   self.w.scale, self.maxc_d, partition_size=self.w.partition_size,
@@ -225,9 +242,10 @@ def evict(flush_buf):
 
 def measure(step, steps, warmup, flush_buf):
     """Event-timed steps over `steps` steps (after `warmup`), in three passes:
-    the step between two events ("step"), the step with an event where the
-    decode begins ("decode": plan + partitions + reduce as one span), and one
-    event after every phase (the phases by name).  Returns ms lists."""
+    the one-call step between two events ("step"), the step as separate calls
+    with an event where the decode begins ("decode": plan + partitions +
+    reduce as one span; "step_separate": the whole of it), and one event
+    after every phase (the phases by name).  Returns ms lists."""
     phases = step.phases()
     for _ in range(warmup):
         flush_buf.zero_()
@@ -237,15 +255,18 @@ def measure(step, steps, warmup, flush_buf):
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     res = {name: [] for name, _ in phases}
     res["step"] = []
-    # 1. The whole step.
+    # 1. The whole step, in its one-call form (the write in the decode's plan launch).
+    for _ in range(warmup):
+        flush_buf.zero_()
+        step.one_call_step()
+    torch.cuda.synchronize()
     evs = []
     t0 = time.perf_counter()
     for _ in range(steps):
         evict(flush_buf)
         e = [ev(), ev()]
         e[0].record()
-        for _, fn in phases:
-            fn()
+        step.one_call_step()
         e[1].record()
         evs.append(e)
     torch.cuda.synchronize()
@@ -267,6 +288,7 @@ def measure(step, steps, warmup, flush_buf):
             evs.append(e)
         torch.cuda.synchronize()
         res["decode"] = [e[1].elapsed_time(e[2]) for e in evs]
+        res["step_separate"] = [e[0].elapsed_time(e[2]) for e in evs]
     # 3. Every phase.
     evs = []
     for _ in range(steps):
@@ -864,7 +886,7 @@ def main():
                    "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "block_size": w.block_size,
                    "context_lens": "uniform[512,4096]", "partition_size": w.partition_size,
-                   "reduce_kernel": True,
+                   "reduce_kernel": True, "step_calls": "pa_decode_fused_write (cache write in the plan launch)",
                    "decode_item_partitions": r.get("decode_plan", {}).get("item_partitions"),
                    "num_blocks": w.num_blocks},
         "hbm_frac": round(r["step_gbs"] / HBM_PEAK_GBS, 4),
