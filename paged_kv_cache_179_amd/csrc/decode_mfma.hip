@@ -749,7 +749,12 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
       // with no pass in a round still keeps its slot parity in step).
       if (lane == 0) s_part[wave] = slot;
       int gs[kWaves];
-      for (int r = 0; r < nround; ++r) {
+      // At least one round (a shared partition is a full one, of at least 64
+      // tokens), written so that the compiler sees the wait below on every
+      // path out of the query loads; otherwise it would wait for them, and so
+      // for every DMA in flight, in the regular units' pass loop.
+      int r = 0;
+      do {
         wait_vmcnt<0>();  // this wave's pass of round r (and at r = 0 its query rows)
         __syncthreads();  // every wave's pass of round r; every wave done with round r - 1
         if (r == 0) {
@@ -766,7 +771,7 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
         for (int w = 0; w < kWaves; ++w)
           if (r * kWaves + w < npass) gpass(reinterpret_cast<const char*>(&s_kv[w][(gs[w] + r) & 1][0][0][0]));
         slot ^= 1;
-      }
+      } while (++r < nround);
       // The next regular unit's query tile has landed before the barrier below.
       if (wave == 0 && nx.valid && !nx.group) {
         if (nx.mine > 0) wait_vmcnt<2 * NDMA>();
@@ -788,9 +793,22 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
   Unit cur = info(u);
   if (!cur.valid) return;  // a static slot past its sequence's context (workgroup-uniform)
   int qb = 0;
-  if (wave == 0 && !cur.group) {
-    issue_q(cur, 0);
-    wait_vmcnt<0>();
+  int slot = 0;
+  if constexpr (KV8) {
+    if (wave == 0 && !cur.group) {
+      issue_q(cur, 0);
+      wait_vmcnt<0>();
+    }
+  } else {
+    // The first pass goes out with the query tile, and only the query tile
+    // is waited for before the barrier: one round trip, not two, before the
+    // first pass can be computed.
+    if (wave == 0 && !cur.group) issue_q(cur, 0);
+    if (cur.mine > 0) issue(cur, 0, slot);
+    if (wave == 0 && !cur.group) {
+      if (cur.mine > 0) wait_vmcnt<2 * NDMA>();
+      else wait_vmcnt<0>();
+    }
   }
   __syncthreads();
   Unit nxt = info(2 * NG - 1 - u);
@@ -857,12 +875,15 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
       const int npass = (x.te - x.tb) / kTile;  // full partition
       const int nround = (npass + kWaves - 1) / kWaves;
       int gs[kWaves];
+      // The query rows, and with them every pass issued so far, have landed
+      // (a wait the compiler sees on every path, so that it adds none of its
+      // own for the query registers inside the rounds).
+      wait_vmcnt<0>();
       for (int r = 0; r < nround; ++r) {
         const bool own = r < x.mine;  // this wave's pass r of x is pass `done` of its stream
         while (issued - done < NS - 1 && issue_next()) {
         }
-        if (r == 0) wait_vmcnt<0>();  // the query rows too
-        else if (own) wait_upto(2 * NDMA * (issued - done - 1) + (wave == 0 && q_after > done ? NQ : 0));
+        if (own) wait_upto(2 * NDMA * (issued - done - 1) + (wave == 0 && q_after > done ? NQ : 0));
         __syncthreads();  // every wave's pass of round r landed; round r - 1 read by every wave
         if (r == 0) {
 #pragma unroll
@@ -933,8 +954,6 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
     }
     return;
   }
-  int slot = 0;
-  if (cur.mine > 0) issue(cur, 0, slot);
   while (true) {
     if (cur.group) {
       group_unit(cur, nxt, slot, qb, queued && nxt.valid);
