@@ -158,7 +158,7 @@ struct PrefillWorkspace {
   size_t bytes;
   size_t off_max, off_sum, off_acc;  // key-range partial states (only when nsplit > 1)
   size_t off_count, off_plan;        // work plan (always)
-  size_t off_tokseq;                 // chunk of each query token, for the merge (only when nsplit > 1)
+  size_t off_toklim;                 // last key of each query token's rows, or -1, for the merge (only when nsplit > 1)
 };
 int32_t prefill_num_splits(int32_t ctx_limit);
 int32_t prefill_num_tiles(int32_t num_heads, int32_t num_kv_heads, int32_t max_query_len);

@@ -161,7 +161,7 @@ constexpr int kPlanSeqCache = 4096;  // chunks whose bounds and context lengths 
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs a, int32_t pos_per_tile,
                                                                    int32_t ntiles, int32_t nsplit,
                                                                    int4* plan, int32_t* plan_count,
-                                                                   int32_t* tok_seq) {
+                                                                   int32_t* tok_lim) {
   __shared__ int hist[kPlanBuckets];
   __shared__ int s_qs[kPlanSeqCache];  // query_start_loc as given
   __shared__ int s_cl[kPlanSeqCache];  // context_lens as given
@@ -180,14 +180,28 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
     }
   }
   __syncthreads();
-  // The chunk of every query token (-1 for tokens outside every chunk), for
-  // the merge kernel; only when key ranges are split.
-  if (tok_seq != nullptr) {
+  // For the merge kernel (only when key ranges are split): the last key of
+  // every query token's rows when those keys span more than one range, else
+  // -1 (tokens outside every chunk or past its attended rows, and rows whose
+  // keys fit one range, which the prefill kernel writes itself).
+  if (tok_lim != nullptr) {
     auto start = [&](int s) { return min(max(cached ? s_qs[s] : a.query_start_loc[s], 0), a.num_q_tokens); };
+    // Token t of chunk s.
+    auto lim = [&](int s, int t) {
+      const int q_begin = start(s);
+      const int q_end = max(q_begin, start(s + 1));
+      const int ctx = max(0, min(cached ? s_cl[s] : a.context_lens[s], a.ctx_limit));
+      const int qlen = min(q_end - q_begin, ctx);
+      const int pos = t - q_begin;
+      if (pos >= qlen) return -1;
+      const int row_lim = ctx - qlen + pos;
+      const int p0 = a.window > 0 ? max(0, row_lim - a.window + 1) / kSplitKeys : 0;
+      return row_lim / kSplitKeys + 1 - p0 > 1 ? row_lim : -1;
+    };
     if (cached) {
       for (int t = tid; t < a.num_q_tokens; t += kPlanThreads) {
         if (t < start(0) || t >= start(S)) {
-          tok_seq[t] = -1;
+          tok_lim[t] = -1;
           continue;
         }
         // The last chunk whose start is <= t (the starts do not decrease).
@@ -196,14 +210,14 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillArgs 
           const int mid = (lo + hi) >> 1;
           if (start(mid) <= t) lo = mid; else hi = mid;
         }
-        tok_seq[t] = lo;
+        tok_lim[t] = lim(lo, t);
       }
     } else {
-      for (int t = tid; t < a.num_q_tokens; t += kPlanThreads) tok_seq[t] = -1;
+      for (int t = tid; t < a.num_q_tokens; t += kPlanThreads) tok_lim[t] = -1;
       __syncthreads();
       for (int s = tid; s < S; s += kPlanThreads) {
         const int b = start(s), e = max(b, start(s + 1));
-        for (int t = b; t < e; ++t) tok_seq[t] = s;
+        for (int t = b; t < e; ++t) tok_lim[t] = lim(s, t);
       }
     }
   }
@@ -882,13 +896,12 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
 }
 
 // One wave per (query token, head): merge the key-range partials of rows
-// whose keys spanned more than one range.  Each wave issues its loads in
-// three rounds (the token's chunk from the plan's map, the chunk's bounds,
-// then up to four ranges' states at once), so the kernel costs a few memory
-// latencies.
+// whose keys spanned more than one range.  Each wave issues its loads in two
+// rounds (the token's last key from the plan's map, then up to four ranges'
+// states at once), so the kernel costs two memory latencies.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(PrefillArgs a, int32_t nsplit,
-                                                                const int32_t* tok_seq,
+                                                                const int32_t* tok_lim,
                                                                 const float* ws_max,
                                                                 const float* ws_sum,
                                                                 const float* ws_acc) {
@@ -897,15 +910,8 @@ __global__ __launch_bounds__(kThreads) void prefill_merge_kernel(PrefillArgs a, 
   const int lane = threadIdx.x & 63;
   if (rowid >= static_cast<int64_t>(a.num_q_tokens) * a.num_heads) return;
   const int t = static_cast<int>(rowid / a.num_heads);
-  const int seq = tok_seq[t];
-  if (seq < 0) return;
-  const int q_begin = min(max(a.query_start_loc[seq], 0), a.num_q_tokens);
-  const int q_end = min(max(a.query_start_loc[seq + 1], q_begin), a.num_q_tokens);
-  const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
-  const int qlen = min(q_end - q_begin, ctx);
-  const int pos = t - q_begin;
-  if (pos >= qlen) return;
-  const int row_lim = ctx - qlen + pos;
+  const int row_lim = tok_lim[t];
+  if (row_lim < 0) return;  // nothing to merge
   // Key ranges holding the row's keys (those of its window, or 0 .. row_lim).
   const int p0 = a.window > 0 ? max(0, row_lim - a.window + 1) / kSplitKeys : 0;
   const int p1 = row_lim / kSplitKeys + 1;
@@ -981,9 +987,9 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
   float* ws_acc = nsplit > 1 ? reinterpret_cast<float*>(base + w.off_acc) : nullptr;
   int4* plan = reinterpret_cast<int4*>(base + w.off_plan);
   int32_t* plan_count = reinterpret_cast<int32_t*>(base + w.off_count);
-  int32_t* tok_seq = nsplit > 1 ? reinterpret_cast<int32_t*>(base + w.off_tokseq) : nullptr;
+  int32_t* tok_lim = nsplit > 1 ? reinterpret_cast<int32_t*>(base + w.off_toklim) : nullptr;
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, a, pos_per_tile, ntiles,
-                     nsplit, plan, plan_count, tok_seq);
+                     nsplit, plan, plan_count, tok_lim);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // An E4M3 cache's K scale folds into the score scale.
@@ -1009,7 +1015,7 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
   if (rows == 0) return hipSuccess;
   if ((rows + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_merge_kernel<E, D>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(kThreads), 0,
-                     stream, a, nsplit, tok_seq, ws_max, ws_sum, ws_acc);
+                     stream, a, nsplit, tok_lim, ws_max, ws_sum, ws_acc);
   return hipGetLastError();
 }
 
@@ -1049,7 +1055,7 @@ PrefillWorkspace prefill_workspace_layout(int32_t num_q_tokens, int32_t num_head
   w.off_plan = off + 256;
   w.bytes = w.off_plan + align256p(static_cast<size_t>(num_seqs) * ntiles * nsplit * sizeof(int4));
   if (nsplit > 1) {
-    w.off_tokseq = w.bytes;
+    w.off_toklim = w.bytes;
     w.bytes += align256p(static_cast<size_t>(num_q_tokens) * sizeof(int32_t));
   }
   return w;

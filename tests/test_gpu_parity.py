@@ -289,6 +289,27 @@ def test_prefill_single_token_rows_match_decode(gpu):
     assert max_err(pre, oracle_decode(w, kc, vc)) <= 1e-2
 
 
+def test_prefill_many_chunks_split_ranges(gpu):
+    """More chunks than the prefill plan keeps in LDS (4,096), some of them
+    with keys over several 1,024-key ranges: the plan's other path for the
+    merge's per-token key limits."""
+    say("prefill 4100 one-token chunks")
+    w = W.small_case(57, num_seqs=4100, ctx_lo=1, ctx_hi=40, num_heads=4, num_kv_heads=2,
+                     head_dim=64, block_size=16, dtype="bf16",
+                     extra_ctx=[1024, 1025, 2048, 2049, 3000, 1, 17])
+    d = to_dev(w, gpu)
+    run_write(w, d)
+    dec = run_decode(w, d)
+    qsl = torch.arange(w.num_seqs + 1, dtype=torch.int32, device=gpu)
+    pre = torch.empty_like(dec)
+    pa.prefill_chunk(pre, d["query_decode"], qsl, d["key_cache"], d["value_cache"], d["bt_decode"],
+                     d["cl_decode"], w.scale, 1, int(w.context_lens.max()))
+    torch.cuda.synchronize()
+    assert float((pre.float() - dec.float()).abs().max()) <= 1e-2
+    kc, vc = written_caches(w)
+    assert max_err(pre, oracle_decode(w, kc, vc)) <= 1e-2
+
+
 def test_partition_size_does_not_change_result(gpu):
     w = W.small_case(41, num_seqs=5, ctx_lo=1, ctx_hi=4000, num_heads=4, num_kv_heads=2,
                      head_dim=64, block_size=16, dtype="fp32", extra_ctx=[4000, 1, 511])
