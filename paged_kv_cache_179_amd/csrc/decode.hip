@@ -238,16 +238,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reduce_kernel(DecodeArg
   const int lane = threadIdx.x & (kWave - 1);
   if (row >= a.num_seqs * a.num_heads) return;
   const int seq = row / a.num_heads;
-  const int ctx = max(0, min(a.context_lens[seq], a.ctx_limit));
-  if (ctx == 0) return;
+  const int64_t base = static_cast<int64_t>(row) * a.num_parts;
+  // Without a window a row's partitions start at 0: lane p's max and sum are
+  // loaded before the row is known to need merging, in the same round trip as
+  // the context length and the plan's counts (lanes past the row's partitions
+  // read states no call wrote, and drop them).
+  float m_spec = -__builtin_inff(), s_spec = 0.f;
+  if (!WIN && lane < a.num_parts) {
+    m_spec = a.ws_max[base + lane];
+    s_spec = a.ws_sum[base + lane];
+  }
+  // Everything the skip test below reads, loaded up front (the shared count
+  // is only meaningful when the plan made group items, and is then written).
+  const int c_raw = a.context_lens[seq];
+  const int span_log2 = a.plan_count[1];
+  const int n_group = a.plan_count[3];
+  const int shared = WIN ? 0 : a.seq_shared[seq];
+  const int ctx = max(0, min(c_raw, a.ctx_limit));
   // Partitions holding the attended tokens (the window's, or all of them).
   const int p0 = WIN ? window_start(a, ctx) / a.part_tokens : 0;
   const int p1 = (ctx - 1) / a.part_tokens + 1;
-  // Rows whose partitions fit one work item were written by the partition
-  // kernel, unless group items computed some of their partitions.
-  if (p1 - p0 <= (1 << a.plan_count[1]) && (WIN || a.plan_count[3] == 0 || a.seq_shared[seq] == 0))
-    return;
-  const int64_t base = static_cast<int64_t>(row) * a.num_parts;
+  // Nothing to do for an empty context (its rows are zeros, written by the
+  // partition kernel) or for rows whose partitions fit one work item, which
+  // the partition kernel wrote, unless group items computed some of their
+  // partitions.  One test, without short-circuits, so that all its loads go
+  // out together.
+  const bool skip = (ctx == 0) | ((p1 - p0 <= (1 << span_log2)) & (WIN | (n_group == 0) | (shared == 0)));
+  if (skip) return;
   typedef float vecf __attribute__((ext_vector_type(PER)));
   vecf num = {};
   float den;
@@ -258,8 +275,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_reduce_kernel(DecodeArg
     // -inf, sum 0, output never written) are read four at a time, their loads
     // issued before any of them is used.
     const bool in = lane < p1 - p0;
-    const float m_l = in ? a.ws_max[base + p0 + lane] : -__builtin_inff();
-    const float s_l = in ? a.ws_sum[base + p0 + lane] : 0.f;
+    const float m_l = !in ? -__builtin_inff() : WIN ? a.ws_max[base + p0 + lane] : m_spec;
+    const float s_l = !in ? 0.f : WIN ? a.ws_sum[base + p0 + lane] : s_spec;
     const float mu = safe_max(across_groups_max<1>(m_l));
     const float f_l = m_l == -__builtin_inff() ? 0.f : exp2_fast(m_l - mu);
     den = across_groups_sum<1>(f_l * s_l);
