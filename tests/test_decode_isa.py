@@ -8,7 +8,8 @@ DMAs.  When it believes some ordinary vector load may still be outstanding
 adds its own `s_waitcnt vmcnt(0)` before the register is reused, and that wait
 also drains every DMA in flight: the pipeline then runs one pass deep.  This
 compiles the kernel's device code as the build does and checks that no score
-MFMA has such a wait in front of it.
+MFMA has such a wait in front of it, and that no decode kernel uses scratch
+(private) memory.
 """
 import re
 import subprocess
@@ -70,3 +71,17 @@ def test_checker_sees_a_drain():
     ok = [l for l in asm if "vmcnt(0)" not in l]
     assert drained_score_mfmas(ok * 12) == []
 
+
+
+def test_no_scratch(device_asm):
+    """No decode kernel spills to scratch memory (its metadata gives a private
+    segment of 0 bytes)."""
+    seen = 0
+    for i, line in enumerate(device_asm):
+        if ".name:" in line and "decode_mfma_kernel" in line:
+            for follow in device_asm[i + 1:i + 12]:
+                if ".private_segment_fixed_size:" in follow:
+                    seen += 1
+                    assert int(follow.split(":")[1]) == 0, line.split()[-1]
+                    break
+    assert seen >= 12
