@@ -55,7 +55,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;   // merge and plan kernels
+constexpr int kMergeWaves = 4;  // merge kernel: rows (one per wave) per workgroup
 constexpr int kRowsPerWg = 128;  // query rows sharing each K/V tile
 // 16-row MFMA tiles per wave: two, except at head_dim 256 where one keeps a
 // wave's registers (accumulators 16 x 256 fp32 per tile) low enough for two
@@ -900,13 +900,13 @@ __global__ __launch_bounds__(prefill_threads(D)) void prefill_kernel(PrefillArgs
 // rounds (the token's last key from the plan's map, then up to four ranges'
 // states at once), so the kernel costs two memory latencies.
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void prefill_merge_kernel(PrefillArgs a, int32_t nsplit,
+__global__ __launch_bounds__(kMergeWaves * 64) void prefill_merge_kernel(PrefillArgs a, int32_t nsplit,
                                                                 const int32_t* tok_lim,
                                                                 const float* ws_max,
                                                                 const float* ws_sum,
                                                                 const float* ws_acc) {
   constexpr int PER = D / 64;
-  const int64_t rowid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t rowid = static_cast<int64_t>(blockIdx.x) * kMergeWaves + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (rowid >= static_cast<int64_t>(a.num_q_tokens) * a.num_heads) return;
   const int t = static_cast<int>(rowid / a.num_heads);
@@ -1013,8 +1013,9 @@ hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream, void* work
   if (err != hipSuccess || nsplit <= 1) return err;
   const int64_t rows = static_cast<int64_t>(a.num_q_tokens) * a.num_heads;
   if (rows == 0) return hipSuccess;
-  if ((rows + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_merge_kernel<E, D>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(kThreads), 0,
+  if ((rows + kMergeWaves - 1) / kMergeWaves > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_merge_kernel<E, D>), dim3(static_cast<unsigned>((rows + kMergeWaves - 1) / kMergeWaves)),
+                     dim3(kMergeWaves * 64), 0,
                      stream, a, nsplit, tok_lim, ws_max, ws_sum, ws_acc);
   return hipGetLastError();
 }
