@@ -781,11 +781,9 @@ hipError_t launch_decode_partitions_write(const DecodeArgs& args, const CacheWri
   const bool mfma = a.dtype != PA_DTYPE_F32 && (a.kv_fp8 || !vector_kernel_forced());
   a.plan_min_items = 0;
   a.share = 0;
+  a.static_plan = 0;
   if (mfma) {
-    // Join partitions while every persistent workgroup still gets a unit.
     const int group = a.num_heads / a.num_kv_heads;
-    const int per = a.num_kv_heads * ((group + 15) / 16);
-    a.plan_min_items = std::max(1, (decode_mfma_grid(a) + per - 1) / per);
     // Shared partitions: whole contexts, one head chunk per KV head, blocks
     // of 16+ tokens (one scalar table read per pass); E4M3 caches only at
     // head_dim 128 (the kernel's only E4M3 form with a group path).
@@ -799,7 +797,6 @@ hipError_t launch_decode_partitions_write(const DecodeArgs& args, const CacheWri
     a.share_vec = (reinterpret_cast<uintptr_t>(a.block_tables) % 16 == 0 && a.max_blocks_per_seq % 4 == 0 &&
                    bpp % 4 == 0) ? 1 : 0;
   }
-  a.static_plan = 0;
   if (mfma) {
     // Small calls: when every (sequence, partition, head chunk) slot has a
     // workgroup of the persistent grid, each workgroup takes the slot its
@@ -809,7 +806,14 @@ hipError_t launch_decode_partitions_write(const DecodeArgs& args, const CacheWri
     // per item, no group items) are written by the partition kernel.
     const int group = a.num_heads / a.num_kv_heads;
     const uint64_t slots = decode_grid(a, (group + 15) / 16);
-    a.static_plan = slots <= static_cast<uint64_t>(decode_mfma_grid(a)) ? 1 : 0;
+    DecodeArgs st = a;  // the grid of the kernel a static launch takes (no group path)
+    st.static_plan = 1;
+    a.static_plan = slots <= static_cast<uint64_t>(decode_mfma_grid(st)) ? 1 : 0;
+    if (!a.static_plan) {
+      // Join partitions while every persistent workgroup still gets a unit.
+      const int per = a.num_kv_heads * ((group + 15) / 16);
+      a.plan_min_items = std::max(1, (decode_mfma_grid(a) + per - 1) / per);
+    }
   }
   const int pthreads = plan_threads(a.num_seqs);
   WriteRows wr{};

@@ -54,6 +54,7 @@
 // are described with their code below.
 #include <algorithm>
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "lds_dma.h"
@@ -186,7 +187,10 @@ struct Unit {
   int moff;         // group: the item's run in a.members (seq = its first member)
 };
 
-template <typename E, int D, typename S, bool KV8>
+// GROUPS: the launch's plan may hold group items (its search for shared
+// partitions ran).  Launches without them use a copy of the kernel with no
+// group path compiled in.
+template <typename E, int D, typename S, bool KV8, bool GROUPS>
 __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_kernel(DecodeArgs a, int32_t head_chunks,
                                                                             S score) {
   constexpr int kWaves = waves_for<D, KV8>();
@@ -210,10 +214,11 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
   // flight (the bytes in flight per wave of the 16-bit kernel).
   constexpr int NS = KV8 ? 3 : 2;
   // Group units (see below) exist for 16-bit caches and for E4M3 caches at
-  // head_dim 128.  At E4M3 64 and 256 the group path's registers crowd the
-  // regular path's (measured with the path compiled in: TinyLlama-shaped fp8
-  // decode 5% slower, Gemma-shaped 2.5%).
-  constexpr bool kGroupUnits = !KV8 || D == 128;
+  // head_dim 128, in launches whose plan may hold them.  Compiled in, the
+  // group path's registers crowd the regular path's: measured at E4M3 64 and
+  // 256, TinyLlama-shaped fp8 decode 5% slower, Gemma-shaped 2.5%; 16-bit
+  // TinyLlama-shaped decode (static plan) 23.5-23.7 against 22.8-23.0 us.
+  constexpr bool kGroupUnits = GROUPS && (!KV8 || D == 128);
   __shared__ u32x4 s_kv[kWaves][NS][2][kTile][CNC];
   // E4M3 caches: each wave's value tile of the pass it computes, widened to
   // 16 bits and rotated as the 16-bit value slots are (keys are widened in
@@ -329,6 +334,10 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
       x.span = span_word & 0xff;
       x.single = (span_word >> 8) & 1;
       x.group = kGroupUnits && ((span_word >> 9) & 1);
+      // A group item in a launch without the group path cannot come from
+      // this library's plan (the host gives both the same flags); dropped
+      // rather than read as a sequence.
+      if (!kGroupUnits && ((span_word >> 9) & 1)) x.valid = false;
       members_n = span_word >> 16;
     }
     x.kvh = r / head_chunks;
@@ -1016,7 +1025,7 @@ __global__ __launch_bounds__((waves_for<D, KV8>() * kWave)) void decode_mfma_ker
 }
 
 // Workgroups of one persistent launch: as many as fit on the device at once.
-template <typename E, int D, typename S, bool KV8>
+template <typename E, int D, typename S, bool KV8, bool GROUPS>
 int persistent_grid() {
   static std::atomic<int> cache[64];
   int dev = 0;
@@ -1025,7 +1034,7 @@ int persistent_grid() {
   if (g > 0) return g;
   int ncu = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) ncu = 1;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D, S, KV8>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<E, D, S, KV8, GROUPS>,
                                                     waves_for<D, KV8>() * kWave, 0) != hipSuccess)
     per_cu = 1;
   g = std::max(1, ncu) * std::max(1, per_cu);
@@ -1033,12 +1042,24 @@ int persistent_grid() {
   return g;
 }
 
+// Whether a launch takes the kernel with the group path: only when the plan
+// searched for shared partitions (no static plan, the share flag set).
+inline bool mfma_groups(const DecodeArgs& a) { return a.static_plan == 0 && a.share != 0; }
+
+template <typename E, int D, typename S, bool KV8>
+int grid_g(bool groups) {
+  if constexpr (!KV8 || D == 128) {
+    if (groups) return persistent_grid<E, D, S, KV8, true>();
+  }
+  return persistent_grid<E, D, S, KV8, false>();
+}
+
 template <typename E, typename S, bool KV8>
-int grid_s(int head_dim) {
+int grid_s(int head_dim, bool groups) {
   switch (head_dim) {
-    case 64: return persistent_grid<E, 64, S, KV8>();
-    case 128: return persistent_grid<E, 128, S, KV8>();
-    default: return persistent_grid<E, 256, S, KV8>();
+    case 64: return grid_g<E, 64, S, KV8>(groups);
+    case 128: return grid_g<E, 128, S, KV8>(groups);
+    default: return grid_g<E, 256, S, KV8>(groups);
   }
 }
 
@@ -1048,7 +1069,8 @@ inline float qk_scale(const DecodeArgs& a) { return a.kv_fp8 ? a.scale * a.k_sca
 template <typename E>
 int grid_e(const DecodeArgs& a) {
   return with_score_map(qk_scale(a), a.softcap, a.window, [&](auto map) {
-    return a.kv_fp8 ? grid_s<E, decltype(map), true>(a.head_dim) : grid_s<E, decltype(map), false>(a.head_dim);
+    return a.kv_fp8 ? grid_s<E, decltype(map), true>(a.head_dim, mfma_groups(a))
+                    : grid_s<E, decltype(map), false>(a.head_dim, mfma_groups(a));
   });
 }
 
@@ -1060,9 +1082,19 @@ hipError_t launch_kv(const DecodeArgs& a, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   with_score_map(qk_scale(a), a.softcap, a.window, [&](auto map) {
     using S = decltype(map);
-    const uint64_t grid = std::min<uint64_t>(n, static_cast<uint64_t>(persistent_grid<E, D, S, KV8>()));
-    hipLaunchKernelGGL((decode_mfma_kernel<E, D, S, KV8>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(waves_for<D, KV8>() * kWave), 0, stream, a, chunks, map);
+    auto go = [&](auto groups) {
+      constexpr bool GR = decltype(groups)::value;
+      const uint64_t grid = std::min<uint64_t>(n, static_cast<uint64_t>(persistent_grid<E, D, S, KV8, GR>()));
+      hipLaunchKernelGGL((decode_mfma_kernel<E, D, S, KV8, GR>), dim3(static_cast<uint32_t>(grid)),
+                         dim3(waves_for<D, KV8>() * kWave), 0, stream, a, chunks, map);
+    };
+    if constexpr (!KV8 || D == 128) {
+      if (mfma_groups(a)) {
+        go(std::true_type{});
+        return 0;
+      }
+    }
+    go(std::false_type{});
     return 0;
   });
   return hipGetLastError();
