@@ -458,7 +458,10 @@ def partition_kernel_name(w):
     if w.dtype == "fp32":
         g = min(8, w.num_heads // w.num_kv_heads)
         return f"decode_partition_kernel<F32,{w.head_dim},{g}>"
-    return f"decode_mfma_kernel<{w.dtype.upper().replace('FP', 'F')},{w.head_dim},ScoreMap<false,false,false>,false>"
+    # The last argument says whether the launch's plan searched for shared
+    # partitions: not for TinyLlama, whose calls take the static plan.
+    groups = "false" if w.name == "tinyllama" else "true"
+    return f"decode_mfma_kernel<{w.dtype.upper().replace('FP', 'F')},{w.head_dim},ScoreMap<false,false,false>,false,{groups}>"
 
 
 def kernel_source_hash():
